@@ -1,0 +1,237 @@
+/*
+ * Plain CPU oracle of one MoE layer's forward pass (float64, scalar loops).
+ * TEST INFRASTRUCTURE ONLY: see oracle.h for the contract and the sources.
+ *
+ * Deliberately simple: no blocking, no fusion, no reordering beyond what the
+ * definitions state.  The only concession to run time is an OpenMP pragma on
+ * independent outer loops (tokens, rows), which does not change any result:
+ * every output element is computed by one thread in a fixed order.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* exact float64 value of element i of a bf16 or fp32 tensor */
+static double ld(int dt, const void* p, int64_t i) {
+    if (dt == ORACLE_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float*)p)[i];
+}
+
+int32_t oracle_capacity(int32_t T, int32_t k, int32_t E, double factor) {
+    /* tokens per expert times the factor, counting each of the k picks */
+    double c = (double)T * (double)k / (double)E * factor;
+    return (int32_t)floor(c);
+}
+
+void oracle_gate(int64_t T, int64_t H, int64_t E, int dt, const void* x, const void* wg,
+                 float* logits) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int64_t h = 0; h < H; ++h) s += ld(dt, x, t * H + h) * ld(dt, wg, e * H + h);
+            logits[t * E + e] = (float)s; /* one rounding to fp32 */
+        }
+    }
+}
+
+/* does expert a (key ka) come before expert b (key kb) in the top-k order? */
+static int before(float ka, int64_t a, float kb, int64_t b) {
+    if (ka > kb) return 1;
+    if (ka < kb) return 0;
+    return a < b; /* equal keys (+0 == -0 included): lower id first */
+}
+
+void oracle_route(int64_t T, int64_t E, int64_t k, const float* logits, const float* bias,
+                  int renormalize, int32_t* ids, double* w, double* margin) {
+    float* key = (float*)malloc((size_t)E * sizeof(float));
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t e = 0; e < E; ++e) {
+            float l = logits[t * E + e];
+            if (bias) l = l + bias[e]; /* a single fp32 addition */
+            key[e] = l;
+            taken[e] = 0;
+        }
+        /* selection: repeatedly take the first expert in (key desc, id asc) order */
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || before(key[e], e, key[best], best)) best = e;
+            }
+            taken[best] = 1;
+            ids[t * k + j] = (int32_t)best;
+        }
+        if (margin) {
+            if (k == E) {
+                margin[t] = INFINITY;
+            } else {
+                int64_t next = -1;
+                for (int64_t e = 0; e < E; ++e) {
+                    if (taken[e]) continue;
+                    if (next < 0 || before(key[e], e, key[next], next)) next = e;
+                }
+                margin[t] = (double)key[ids[t * k + k - 1]] - (double)key[next];
+            }
+        }
+        /* softmax over all experts: p_e = exp(l'_e - m) / sum_e' exp(l'_e' - m) */
+        double m = (double)key[ids[t * k]];
+        double full = 0.0;
+        for (int64_t e = 0; e < E; ++e) full += exp((double)key[e] - m);
+        double picked = 0.0;
+        for (int64_t j = 0; j < k; ++j) picked += exp((double)key[ids[t * k + j]] - m) / full;
+        for (int64_t j = 0; j < k; ++j) {
+            double p = exp((double)key[ids[t * k + j]] - m) / full;
+            w[t * k + j] = renormalize ? p / picked : p;
+        }
+    }
+    free(key);
+    free(taken);
+}
+
+int64_t oracle_permute(int64_t T, int64_t E, int64_t k, int32_t capacity, const int32_t* ids,
+                       const uint8_t* active, int32_t* raw, int32_t* counts, int32_t* offsets,
+                       int32_t* row_token, int32_t* pos, uint8_t* dropped) {
+    /* buckets: for each expert, its (token, slot) entries in ascending token order */
+    int64_t n = T * k;
+    int64_t* bucket_slot = (int64_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+    int64_t* bucket_start = (int64_t*)calloc((size_t)E + 1, sizeof(int64_t));
+    int64_t* fill = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t e = 0; e < E; ++e) raw[e] = 0;
+    for (int64_t s = 0; s < n; ++s)
+        if (!active || active[s]) raw[ids[s]]++;
+    for (int64_t e = 0; e < E; ++e) bucket_start[e + 1] = bucket_start[e] + raw[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t s = t * k + j;
+            if (active && !active[s]) continue;
+            int64_t e = ids[s];
+            bucket_slot[bucket_start[e] + fill[e]++] = s;
+        }
+    /* capacity: keep the first `capacity` entries of each bucket */
+    int64_t n_dropped = 0;
+    for (int64_t s = 0; s < n; ++s) {
+        pos[s] = -1;
+        dropped[s] = 1;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t kept = raw[e];
+        if (capacity >= 0 && kept > capacity) kept = capacity;
+        counts[e] = (int32_t)kept;
+        offsets[e + 1] = offsets[e] + (int32_t)kept;
+        n_dropped += raw[e] - kept;
+        for (int64_t r = 0; r < kept; ++r) {
+            int64_t s = bucket_slot[bucket_start[e] + r];
+            int32_t row = offsets[e] + (int32_t)r;
+            row_token[row] = (int32_t)(s / k);
+            pos[s] = row;
+            dropped[s] = 0;
+        }
+    }
+    free(bucket_slot);
+    free(bucket_start);
+    free(fill);
+    return n_dropped;
+}
+
+static double silu(double a) { return a / (1.0 + exp(-a)); }
+
+void oracle_expert_ffn(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr, int dt_w,
+                       const void* w1, const void* w3, const void* w2, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        double* h = (double*)malloc((size_t)I * sizeof(double));
+        for (int64_t i = 0; i < I; ++i) {
+            double a = 0.0, g = 0.0;
+            for (int64_t c = 0; c < H; ++c) {
+                double xv = ld(dt_x, xr, m * H + c);
+                a += ld(dt_w, w1, i * H + c) * xv;
+                g += ld(dt_w, w3, i * H + c) * xv;
+            }
+            h[i] = silu(a) * g;
+        }
+        for (int64_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int64_t i = 0; i < I; ++i) s += ld(dt_w, w2, c * I + i) * h[i];
+            out[m * H + c] = s;
+        }
+        free(h);
+    }
+}
+
+void oracle_combine(int64_t T, int64_t H, int64_t k, const double* yp, const int32_t* pos,
+                    const double* w, const double* ys, double* y) {
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int64_t j = 0; j < k; ++j) {
+                int32_t r = pos[t * k + j];
+                if (r >= 0) s += w[t * k + j] * yp[(int64_t)r * H + c];
+            }
+            if (ys) s += ys[t * H + c];
+            y[t * H + c] = s;
+        }
+    }
+}
+
+int64_t oracle_layer(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is,
+                     int32_t capacity, int renormalize, int dt, const void* x, const void* wg,
+                     const float* bias, const void* w1, const void* w3, const void* w2,
+                     const void* ws1, const void* ws3, const void* ws2, double* y,
+                     float* logits_out, int32_t* ids_out, double* w_out, int32_t* pos_out,
+                     int32_t* counts_out) {
+    int64_t n = T * k;
+    size_t es = dt == ORACLE_BF16 ? 2 : 4;
+    float* logits = (float*)malloc((size_t)(T * E > 0 ? T * E : 1) * sizeof(float));
+    int32_t* ids = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    double* w = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    int32_t* raw = (int32_t*)malloc((size_t)E * sizeof(int32_t));
+    int32_t* counts = (int32_t*)malloc((size_t)E * sizeof(int32_t));
+    int32_t* offsets = (int32_t*)malloc((size_t)(E + 1) * sizeof(int32_t));
+    int32_t* row_token = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    int32_t* pos = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    uint8_t* dropped = (uint8_t*)malloc((size_t)(n > 0 ? n : 1));
+    double* yp = (double*)malloc((size_t)(n > 0 ? n : 1) * (size_t)H * sizeof(double));
+    double* ys = NULL;
+
+    oracle_gate(T, H, E, dt, x, wg, logits);
+    oracle_route(T, E, k, logits, bias, renormalize, ids, w, NULL);
+    int64_t n_dropped =
+        oracle_permute(T, E, k, capacity, ids, NULL, raw, counts, offsets, row_token, pos, dropped);
+
+    /* each expert runs on the rows gathered for it (the packed x) */
+    char* xp = (char*)malloc((size_t)(n > 0 ? n : 1) * (size_t)H * es);
+    for (int64_t r = 0; r < offsets[E]; ++r)
+        memcpy(xp + (size_t)r * H * es, (const char*)x + (size_t)row_token[r] * H * es, (size_t)H * es);
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t rows = counts[e];
+        if (!rows) continue;
+        oracle_expert_ffn(rows, H, I, dt, xp + (size_t)offsets[e] * H * es, dt,
+                          (const char*)w1 + (size_t)e * I * H * es,
+                          (const char*)w3 + (size_t)e * I * H * es,
+                          (const char*)w2 + (size_t)e * H * I * es, yp + (size_t)offsets[e] * H);
+    }
+    if (Is > 0) {
+        ys = (double*)malloc((size_t)(T > 0 ? T : 1) * (size_t)H * sizeof(double));
+        oracle_expert_ffn(T, H, Is, dt, x, dt, ws1, ws3, ws2, ys);
+    }
+    oracle_combine(T, H, k, yp, pos, w, ys, y);
+
+    if (logits_out) memcpy(logits_out, logits, (size_t)T * E * sizeof(float));
+    if (ids_out) memcpy(ids_out, ids, (size_t)n * sizeof(int32_t));
+    if (w_out) memcpy(w_out, w, (size_t)n * sizeof(double));
+    if (pos_out) memcpy(pos_out, pos, (size_t)n * sizeof(int32_t));
+    if (counts_out) memcpy(counts_out, counts, (size_t)E * sizeof(int32_t));
+    free(logits); free(ids); free(w); free(raw); free(counts); free(offsets);
+    free(row_token); free(pos); free(dropped); free(yp); free(xp); free(ys);
+    return n_dropped;
+}

@@ -1,0 +1,101 @@
+/*
+ * Plain CPU oracle of one MoE layer's forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU path shares no
+ * code with it: no header, no helper, no table.
+ *
+ * Every function is a direct transcription of the layer's definition as the
+ * pages state it, in scalar loops with float64 arithmetic over the exact input
+ * values (bf16 inputs are widened exactly; fp32 inputs are read as they are).
+ * The router's decisions are taken on fp32 logits, as the GPU takes them, so
+ * that both sides can be given the same logits and compared bit for bit.
+ *
+ * Sources (page titles as printed on the pages):
+ *  [P1] "MoE 推理中的 Expert Parallel、KV Cache 与大规模专家并行架构解析"
+ *  [P3] "MoE 推理架构深度实战：从 Expert Parallelism 到 DeepSeek-V3 的工程落地"
+ *
+ * Parity pins (see tests/test_oracle_*.py): brute-force routing and bucket
+ * permutation in pure Python, closed-form routing weights, the permute/unpermute
+ * identity, a dense all-experts-then-mask reference, textbook SwiGLU closed
+ * forms (silu(ln 3) = 0.75 ln 3), invariants (weights sum to 1, counts sum to
+ * T*k minus drops).  Agreement with numbers printed on the pages cannot be
+ * pinned: the pages print no worked numeric example of the layer.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage type of a tensor argument */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Expert capacity, [P3] §2.1 (router sketch, capacity = tokens / experts x
+ * factor), with the top-k factor included: floor(T*k/E*factor) in double. */
+int32_t oracle_capacity(int32_t T, int32_t k, int32_t E, double factor);
+
+/* Router gate, [P3] §2.1: a bias-free linear map hidden -> experts.
+ * logits[t,e] = fp32( sum_h x[t,h] * wg[e,h] ), summed in float64.
+ * x is [T,H], wg is [E,H] (out x in), both of storage type `dt`. */
+void oracle_gate(int64_t T, int64_t H, int64_t E, int dt, const void* x, const void* wg,
+                 float* logits);
+
+/* Softmax, top-k and renormalisation, [P3] §2.1; [P1] §2 (normalised weights).
+ * keys l'[t,e] = logits[t,e] (+ bias[e] as one fp32 add when bias != NULL).
+ * ids[t, 0..k-1]: the k experts with the largest key, largest first; equal keys
+ * order by lower expert id (+0 and -0 are equal keys).
+ * w[t,j]: softmax of the keys over all experts taken at ids[t,j]; with
+ * renormalize != 0 divided by the sum of the k selected probabilities.
+ * margin[t] (optional): key of the k-th minus key of the (k+1)-th expert in
+ * float64, +inf when k == E. */
+void oracle_route(int64_t T, int64_t E, int64_t k, const float* logits, const float* bias,
+                  int renormalize, int32_t* ids, double* w, double* margin);
+
+/* Count, capacity drop, sort and pack, [P1] §8 (count, sort and pack by target
+ * expert); [P3] §3.1 (grouping by expert id; per-expert buckets filled in
+ * token order).  Assignments of expert e are bucketed in ascending token
+ * order; with capacity >= 0 only the first `capacity` of each bucket are kept.
+ * raw[e] bucket sizes before the drop, counts[e] kept sizes,
+ * offsets[E+1] exclusive prefix sum of counts, row_token[offsets[e] + r] the
+ * token of the r-th kept entry of e, pos[t,j] its row or -1 when dropped,
+ * dropped[t,j] 1 when dropped.  `active` (optional, [T*k]) marks which slots
+ * take part at all; an inactive slot is treated as dropped without counting
+ * against capacity.  Returns the number of dropped active slots. */
+int64_t oracle_permute(int64_t T, int64_t E, int64_t k, int32_t capacity, const int32_t* ids,
+                       const uint8_t* active, int32_t* raw, int32_t* counts, int32_t* offsets,
+                       int32_t* row_token, int32_t* pos, uint8_t* dropped);
+
+/* One expert's SwiGLU FFN on M rows, [P1] §1 (FFN(x) = W2 s(W1 x) with an added
+ * gate projection) and §2 (input and output of hidden size, inner size I):
+ * out[m,:] = W2 ( silu(W1 x_m) * (W3 x_m) ), silu(a) = a / (1 + exp(-a)).
+ * xr [M,H] storage `dt_x`; w1, w3 [I,H] and w2 [H,I] storage `dt_w`;
+ * out [M,H] float64. */
+void oracle_expert_ffn(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr, int dt_w,
+                       const void* w1, const void* w3, const void* w2, double* out);
+
+/* Weighted combine and restore of token order, [P1] §2 (y = sum of g_i E_i(x))
+ * and §7 (outputs return to their tokens, weighted by the router).
+ * y[t,:] = sum over j ascending with pos[t,j] >= 0 of w[t,j] * yp[pos[t,j],:]
+ *          (+ ys[t,:] when ys != NULL, the always-on expert with weight 1). */
+void oracle_combine(int64_t T, int64_t H, int64_t k, const double* yp, const int32_t* pos,
+                    const double* w, const double* ys, double* y);
+
+/* The whole layer on small inputs: gate, route, permute, per-expert FFN,
+ * combine.  w1, w3 [E,I,H]; w2 [E,H,I]; ws1, ws3 [Is,H], ws2 [H,Is] or NULL
+ * (Is = 0).  Optional outputs (NULL to skip): logits, ids, w, pos, counts.
+ * Returns the number of dropped slots. */
+int64_t oracle_layer(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is,
+                     int32_t capacity, int renormalize, int dt, const void* x, const void* wg,
+                     const float* bias, const void* w1, const void* w3, const void* w2,
+                     const void* ws1, const void* ws3, const void* ws2, double* y,
+                     float* logits_out, int32_t* ids_out, double* w_out, int32_t* pos_out,
+                     int32_t* counts_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,70 @@
+"""Step-wise use of the CPU oracle on a workload, generating only the experts it needs.
+
+Test infrastructure: every number here comes from ``oracle`` (the C oracle) or
+from ``moe_synth`` (the seeded inputs); this module only sequences the calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import moe_synth
+import oracle
+
+
+class Weights:
+    """Lazily drawn expert weights of a workload (cached per expert)."""
+
+    def __init__(self, w: moe_synth.Workload, cache: bool = True):
+        self.w = w
+        self.cache = cache
+        self._e = {}
+
+    def expert(self, e):
+        if e in self._e:
+            return self._e[e]
+        t = moe_synth.expert_weights(self.w, e)
+        if self.cache:
+            self._e[e] = t
+        return t
+
+
+def routing(w: moe_synth.Workload, x=None, logits=None):
+    """Oracle gate (unless logits are given), route and permute for workload w."""
+    if logits is None:
+        logits = oracle.gate(x, moe_synth.gate_weight(w))
+    bias = moe_synth.logit_bias(w)
+    ids, wts, margin = oracle.route(logits, w.k, bias=bias, renormalize=w.renormalize)
+    cap = oracle.capacity(logits.shape[0], w.k, w.E, w.capacity_factor)
+    perm = oracle.permute(ids, w.E, cap)
+    return dict(logits=logits, ids=ids, w=wts, margin=margin, capacity=cap, **perm)
+
+
+def layer_tokens(w: moe_synth.Workload, x, route, tokens, weights: Weights, shared=None):
+    """float64 outputs y[tokens] of the layer, given the oracle's full routing.
+
+    Runs each needed expert only on the selected tokens' kept slots and sums in
+    slot order (oracle.combine); the always-on expert is added when present.
+    """
+    tokens = np.asarray(tokens, np.int64)
+    n, k, H = len(tokens), w.k, w.H
+    pos = route["pos"][tokens]
+    ids = route["ids"][tokens]
+    wts = route["w"][tokens]
+    yp = np.zeros((n * k, H))
+    sub_pos = np.full((n, k), -1, np.int32)
+    need = {}
+    for i in range(n):
+        for j in range(k):
+            if pos[i, j] >= 0:
+                need.setdefault(int(ids[i, j]), []).append((i, j))
+    for e, lst in sorted(need.items()):
+        w1, w3, w2 = weights.expert(e)
+        rows = np.stack([x[tokens[i]] for (i, j) in lst])
+        out = oracle.expert_ffn(rows, w1, w3, w2)
+        for r, (i, j) in enumerate(lst):
+            yp[i * k + j] = out[r]
+            sub_pos[i, j] = i * k + j
+    ys = None
+    if shared is not None:
+        ys = oracle.expert_ffn(x[tokens], *shared)
+    return oracle.combine(yp, sub_pos, wts, ys)
