@@ -1,0 +1,194 @@
+"""Benchmark of the fused MoE-layer forward on one MI355X.
+
+One step = one moe_layer_forward (gate, softmax/top-k/renormalise, count/scan/
+scatter, grouped SwiGLU gate-up + down, weighted combine) over one batch of
+seeded synthetic tokens already resident in HBM.  Prints one JSON line.
+
+The default workload is the Mixtral-shaped prefill (T4096 H4096 E8 k2 I14336,
+bf16 storage, fp32 accumulation).  --workload picks another of the seeded
+workloads for exploration.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+METRIC = "MoE-layer tokens/s on 1 GPU; MFMA % peak (prefill), HBM GB/s % peak (decode)"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_scatter_amd as moe
+    from mixture_experts_layer_scatter_amd import _lib
+    from mixture_experts_layer_scatter_amd.hip_events import Event
+    import moe_synth
+    from moe_synth.device import workload_tensors
+
+    w = moe_synth.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} Is={w.I_shared} {w.dtype}")
+    t = workload_tensors(w, device=dev, log=log)
+    cap = -1 if w.capacity_factor is None else moe.capacity(w.T, w.k, w.E, w.capacity_factor)
+    d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, I_shared=w.I_shared, capacity=cap,
+                 renormalize=w.renormalize, dtype=w.dtype)
+    ws = moe.workspace(d, dev)
+    y = torch.empty((w.T, w.H), dtype=d.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(debug=None):
+        moe.layer_forward(d, t["x"], t["wg"], t["bias"], t["w1"], t["w3"], t["w2"], t["shared"],
+                          y=y, ws=ws, debug=debug)
+
+    # routing statistics (one extra untimed run)
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    step(dict(counts=counts, n_dropped=nd))
+    torch.cuda.synchronize()
+    cnt = counts.cpu().numpy().astype(np.int64)
+    R = int(cnt.sum())
+    touched = int((cnt > 0).sum())
+    n_dropped = int(nd.item())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: events around the dominant kernel on the launch stream
+    dom = (_lib.EV_PERMUTE, _lib.EV_GATE_UP)
+    pairs = [(Event(), Event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        ev = [None] * _lib.NUM_EVENTS
+        ev[dom[0]], ev[dom[1]] = a.handle.value, b.handle.value
+        step(dict(events=ev))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu_ms = [a.elapsed_ms(b) for a, b in pairs]
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-stage breakdown (untimed extra steps)
+    stage = [Event() for _ in range(_lib.NUM_EVENTS)]
+    stage_ms = np.zeros(_lib.NUM_EVENTS - 1)
+    for _ in range(5):
+        step(dict(events=[e.handle.value for e in stage]))
+        stage[-1].synchronize()
+        stage_ms += [stage[i].elapsed_ms(stage[i + 1]) for i in range(_lib.NUM_EVENTS - 1)]
+    stage_ms /= 5
+    names = ["gate", "route", "permute", "gate_up", "down", "combine"]
+
+    es = 2 if w.dtype == "bf16" else 4
+    Is = w.I_shared
+    F = 2.0 * w.T * w.H * w.E + 6.0 * R * w.H * w.I + 6.0 * w.T * w.H * Is
+    B = (3.0 * w.H * w.I * es * touched + 3.0 * w.H * Is * es + w.E * w.H * es
+         + 2.0 * w.T * w.H * es)
+    gu_avg = float(np.mean(gu_ms))
+    decode = w.name == "dsv3_decode" or (R / max(touched, 1)) < 64
+    if decode:
+        # gate-up streams W1 and W3 of every touched expert (and the shared expert) once
+        gu_bytes = 2.0 * w.H * w.I * es * touched + 2.0 * w.H * Is * es + w.T * w.H * es
+        achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        gu_flops = 4.0 * R * w.H * w.I + 4.0 * w.T * w.H * Is
+        achieved = gu_flops / (gu_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "gemm_bf16_kernel (grouped gate-up + SiLU*mul)"
+    roof["avg_launch_ms"] = round(gu_avg, 4)
+    layer_s = ms_per_step * 1e-3
+    layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.T / layer_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal draws, shapes of the named workload)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
+                   "I_shared": Is, "capacity": cap, "accumulate": "fp32"},
+        "roofline": roof,
+        "layer": {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
+                  "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
+                  "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
+                  "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
+                  "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())]},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, target_s):
+    """The oracle (plain float64 C loops) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import moe_synth
+    import oracle
+
+    log("cpu baseline: drawing host weights")
+    x_all = moe_synth.x(w)
+    wg = moe_synth.gate_weight(w)
+    W1, W3, W2 = moe_synth.all_expert_weights(w)
+    sh = moe_synth.shared_weights(w)
+    bias = moe_synth.logit_bias(w)
+    threads = oracle.threads()
+    n = 4
+    while True:
+        xs = np.ascontiguousarray(x_all[:n])
+        cap = oracle.capacity(n, w.k, w.E, w.capacity_factor)
+        t0 = time.perf_counter()
+        oracle.layer(xs, wg, W1, W3, W2, k=w.k, capacity=cap, renormalize=w.renormalize,
+                     bias=bias, shared=sh)
+        dt = time.perf_counter() - t0
+        log(f"cpu baseline: {n} tokens in {dt:.2f} s on {threads} threads")
+        if dt >= target_s / 3 or n >= w.T:
+            break
+        n = min(w.T, max(n * 2, int(n * target_s / max(dt, 1e-3) / 2)))
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the same workload, whole layer "
+                      f"(gate, route, permute, expert FFNs, combine) in float64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * moe.h: C ABI of libmoe.so, the forward pass of one Mixture-of-Experts layer
+ * on one AMD Instinct MI355X (gfx950), hand-written in HIP.
+ *
+ * Sources (cited by page title and section):
+ *  [P1] "MoE 推理中的 Expert Parallel、KV Cache 与大规模专家并行架构解析"
+ *  [P2] "MoE Expert Parallelism 实战：稀疏大模型推理的通信与负载均衡治理"
+ *  [P3] "MoE 推理架构深度实战：从 Expert Parallelism 到 DeepSeek-V3 的工程落地"
+ *
+ * The layer: a router (bias-free linear gate, softmax, top-k, renormalise),
+ * then tokens counted, sorted and packed by expert, then each expert's SwiGLU
+ * FFN run as one grouped GEMM over its rows, then the routing-weighted combine
+ * back into token order ([P1] §2, §7, §8; [P2] "核心原理" §1; [P3] §2.1).
+ * On one GPU the pack step stands in for the expert-parallel all-to-all.
+ *
+ * Conventions shared by every call:
+ *  - Every array pointer is a DEVICE pointer; the caller allocates and owns it.
+ *    The library never allocates, frees or retains a pointer after a call
+ *    returns.  Scratch memory comes from the caller's workspace (`ws`,
+ *    `ws_bytes`), sized by moe_workspace_bytes().
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work and return; outputs are ready when the stream reaches that point.
+ *    No call synchronises with the host.
+ *  - Layouts are row-major and contiguous.  Weights use the [out, in] layout
+ *    of a linear layer, so both GEMM operands are contiguous along the
+ *    reduction dimension.
+ *  - `dtype` (MOE_F32 or MOE_BF16) is the storage type of x, the weights, the
+ *    packed rows and y.  Accumulation is always fp32; logits and routing
+ *    weights are always fp32; ids, counts, offsets and positions are int32.
+ *  - Arguments are checked on the host before anything is launched.  On error
+ *    nothing is launched and outputs are untouched.  No C++ exception crosses
+ *    the ABI.  T = 0 is a valid no-op.
+ *  - Deterministic: identical inputs give bitwise-identical outputs (no
+ *    floating-point atomics; every sum has a fixed order).
+ *  - Thread-safe: the library holds no mutable global state.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL required pointer, k < 1, k > E, negative size, ... */
+  MOE_ERR_UNSUPPORTED = 2, /* a size outside what the kernels handle (see moe_dims_t)   */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_bytes()               */
+  MOE_ERR_HIP = 4          /* a HIP runtime error while enqueuing                       */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Layer dimensions.
+ *  T  tokens (>= 0), H hidden size, E routed experts (1..1024), k top-k (1..E),
+ *  I  expert intermediate size.  I_shared: 0, or the intermediate size of one
+ *  always-on shared expert added to every token with weight 1 ([P1] §3 names
+ *  shared experts beside routed ones; the weight is a reading).
+ *  capacity: < 0 unlimited; >= 0 the most rows one expert keeps, extra
+ *  assignments dropped in token order (see moe_capacity).
+ *  renormalize: 1 = divide the k picked probabilities by their sum ([P3]
+ *  §2.1); 0 = keep the raw softmax probabilities.
+ *  Supported: bf16 needs H % 64 == 0, I % 64 == 0 and I_shared % 64 == 0;
+ *  fp32 needs H % 4 == 0.  T * k must fit in int32. */
+typedef struct {
+  int32_t T, H, E, k, I;
+  int32_t I_shared;
+  int32_t capacity;
+  int32_t renormalize;
+  int32_t dtype; /* moe_dtype_t */
+} moe_dims_t;
+
+/* Stage boundaries of moe_layer_forward at which events can be recorded. */
+enum {
+  MOE_EV_START = 0,      /* before the gate                                   */
+  MOE_EV_GATE = 1,       /* after the gate GEMM                               */
+  MOE_EV_ROUTE = 2,      /* after softmax / top-k / renormalise               */
+  MOE_EV_PERMUTE = 3,    /* after count / scan / scatter and the tile maps    */
+  MOE_EV_GATE_UP = 4,    /* after the grouped gate-up GEMM (+ SiLU*mul)       */
+  MOE_EV_DOWN = 5,       /* after the grouped down GEMM                       */
+  MOE_EV_END = 6,        /* after the combine (and a separate shared expert)  */
+  MOE_NUM_EVENTS = 7
+};
+
+/* Optional debug outputs of moe_layer_forward; any pointer may be NULL.
+ * events[i], when non-NULL, is a hipEvent_t the call records on `stream` at
+ * stage boundary i (per-stage timing; the caller creates and owns the
+ * events). */
+typedef struct {
+  float* logits;     /* [T,E] gate logits (before the bias)          */
+  int32_t* topk_ids; /* [T,k]                                         */
+  float* topk_w;     /* [T,k]                                         */
+  int32_t* counts;   /* [E]   kept rows per expert                    */
+  int32_t* offsets;  /* [E+1] exclusive prefix sum of counts          */
+  int32_t* pos;      /* [T,k] packed row of each slot, -1 if dropped  */
+  int32_t* n_dropped;/* [1]                                           */
+  void* events[MOE_NUM_EVENTS];
+} moe_debug_out_t;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(int32_t status);
+
+/* Expert capacity, host-side: floor(T * k / E * factor) in double.
+ * [P3] §2.1 gives capacity as tokens / experts times a factor (1.25 in
+ * training, 2.0 in evaluation); the factor k counts every pick of a token
+ * (a reading: without it a top-2 layer could keep only half its picks).
+ * Returns -1 when E <= 0 or factor < 0. */
+int32_t moe_capacity(int32_t T, int32_t k, int32_t E, double factor);
+
+/* Workspace bytes that any call below needs for `dims` (the maximum over all
+ * calls; the same workspace serves each of them).  0 on invalid dims. */
+size_t moe_workspace_bytes(const moe_dims_t* dims);
+
+/* Router gate, [P3] §2.1: logits = x * Wg^T, a linear map without bias.
+ *  x [T,H] (dtype), wg [E,H] (dtype) -> logits [T,E] fp32.
+ *  bf16 runs on MFMA (fp32 accumulate); fp32 on vector FMA. */
+moe_status_t moe_gate(const moe_dims_t* dims, const void* x, const void* wg, float* logits,
+                      void* stream);
+
+/* Softmax, top-k, renormalisation and capacity drop, [P3] §2.1.
+ *  logits [T,E] fp32; bias [E] fp32 or NULL, added to the logits (one fp32
+ *  add) before the softmax and the selection.
+ *  topk_ids [T,k]: the k experts with the largest key, largest first; equal
+ *  keys (+0 == -0) go to the lower expert id.
+ *  topk_w [T,k]: their softmax probabilities, renormalised over the k picks
+ *  when dims->renormalize.
+ *  counts [E] (or NULL): rows each expert keeps after the capacity drop.
+ *  dropped [T,k] u8 (or NULL): 1 where the slot was dropped (capacity reached
+ *  by earlier tokens of that expert).  n_dropped [1] (or NULL).
+ *  A non-NULL counts, dropped or n_dropped needs the workspace. */
+moe_status_t moe_route(const moe_dims_t* dims, const float* logits, const float* bias,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, uint8_t* dropped,
+                       int32_t* n_dropped, void* ws, size_t ws_bytes, void* stream);
+
+/* Count, exclusive prefix sum and stable scatter into expert-contiguous rows,
+ * [P1] §8 (count, sort and pack by target expert); [P3] §3.1 (group by
+ * expert id, token order kept inside each expert).
+ *  topk_ids [T,k]; dropped [T,k] u8 or NULL (NULL = keep every slot).
+ *  offsets [E+1]: offsets[e] is the first packed row of expert e, offsets[E]
+ *  the number of kept rows R.
+ *  row_token [T*k]: the source token of each packed row (first R valid).
+ *  pos [T,k]: the packed row of each slot, -1 if dropped.
+ *  x_packed [T*k,H] (dtype) or NULL: rows of x gathered in packed order.
+ *  x may be NULL when x_packed is NULL. */
+moe_status_t moe_permute(const moe_dims_t* dims, const void* x, const int32_t* topk_ids,
+                         const uint8_t* dropped, int32_t* offsets, int32_t* row_token,
+                         int32_t* pos, void* x_packed, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU expert FFN, [P1] §1 (FFN with an added gate projection), §2
+ * (hidden size in and out, intermediate size inside) and §8 (one grouped GEMM
+ * over the tokens each expert collected).
+ *  For each expert e and packed row r in [offsets[e], offsets[e+1]):
+ *  y_packed[r] = W2[e] ( silu(W1[e] x_packed[r]) * (W3[e] x_packed[r]) ),
+ *  silu(a) = a / (1 + exp(-a)).
+ *  x_packed [T*k,H], w1 [E,I,H], w3 [E,I,H], w2 [E,H,I], y_packed [T*k,H]
+ *  (all dtype); offsets [E+1] on the device (as moe_permute writes them).
+ *  The intermediate activation lives in the workspace (bf16 for bf16).
+ *  Rows past offsets[E] are not written. */
+moe_status_t moe_expert_ffn(const moe_dims_t* dims, const void* x_packed, const int32_t* offsets,
+                            const void* w1, const void* w3, const void* w2, void* y_packed,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine and restore of token order, [P1] §2 and §7; [P2] "核心原理"
+ * §1 (outputs merged back into the original token order).
+ *  y[t] = sum over j = 0..k-1 with pos[t,j] >= 0 of topk_w[t,j] * y_packed[pos[t,j]]
+ *         (+ y_shared[t] when y_shared != NULL),
+ *  summed in fp32 in slot order, rounded once to dtype.
+ *  y_packed [*,H], pos [T,k], topk_w [T,k], y_shared [T,H] or NULL, y [T,H]. */
+moe_status_t moe_combine(const moe_dims_t* dims, const void* y_packed, const int32_t* pos,
+                         const float* topk_w, const void* y_shared, void* y, void* stream);
+
+/* The whole layer in one enqueue: gate, route (+bias, capacity), permute,
+ * grouped gate-up with SiLU*mul, grouped down, combine.  The pack is fused into
+ * the gate-up GEMM's row loads.  The shared expert (dims->I_shared > 0) runs
+ * as one more group over all T tokens.
+ *  x [T,H], wg [E,H], bias [E] fp32 or NULL, w1/w3 [E,I,H], w2 [E,H,I],
+ *  ws1/ws3 [I_shared,H], ws2 [H,I_shared] (NULL when I_shared == 0), y [T,H].
+ *  dbg: NULL, or a struct whose non-NULL members receive intermediates. */
+moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg,
+                               const float* bias, const void* w1, const void* w3, const void* w2,
+                               const void* ws1, const void* ws3, const void* ws2, void* y,
+                               const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,9 @@
+"""MI355X-native forward pass of one Mixture-of-Experts layer (HIP, gfx950).
+
+The compute lives in libmoe.so (C ABI in include/moe.h); this package holds its
+thin torch binding.  Submodules load the library on first use and raise when it
+has not been built.
+"""
+from ._lib import LIB_PATH, MoeError, EXPORTS  # noqa: F401
+from .api import (Dims, capacity, combine, expert_ffn, gate, layer_forward, permute,  # noqa: F401
+                  route, workspace, workspace_bytes)

@@ -1,0 +1,77 @@
+"""ctypes declarations of libmoe.so (include/moe.h).  Loading fails loudly when
+the library has not been built: there is no fallback path."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+# every symbol include/moe.h declares
+EXPORTS = ("moe_status_str", "moe_capacity", "moe_workspace_bytes", "moe_gate", "moe_route",
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+
+
+class MoeDims(C.Structure):
+    _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
+                ("I", C.c_int32), ("I_shared", C.c_int32), ("capacity", C.c_int32),
+                ("renormalize", C.c_int32), ("dtype", C.c_int32)]
+
+
+class MoeDebugOut(C.Structure):
+    _fields_ = [("logits", C.c_void_p), ("topk_ids", C.c_void_p), ("topk_w", C.c_void_p),
+                ("counts", C.c_void_p), ("offsets", C.c_void_p), ("pos", C.c_void_p),
+                ("n_dropped", C.c_void_p), ("events", C.c_void_p * 7)]
+
+# stage boundaries of moe_layer_forward (MOE_EV_* in include/moe.h)
+EV_START, EV_GATE, EV_ROUTE, EV_PERMUTE, EV_GATE_UP, EV_DOWN, EV_END, NUM_EVENTS = range(8)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "(hipcc, gfx950) first")
+        L = C.CDLL(LIB_PATH)
+        p, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        D = C.POINTER(MoeDims)
+        L.moe_status_str.restype = C.c_char_p
+        L.moe_status_str.argtypes = [i32]
+        L.moe_capacity.restype = i32
+        L.moe_capacity.argtypes = [i32, i32, i32, C.c_double]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_bytes.argtypes = [D]
+        L.moe_gate.restype = i32
+        L.moe_gate.argtypes = [D, p, p, p, p]
+        L.moe_route.restype = i32
+        L.moe_route.argtypes = [D, p, p, p, p, p, p, p, p, sz, p]
+        L.moe_permute.restype = i32
+        L.moe_permute.argtypes = [D, p, p, p, p, p, p, p, p, sz, p]
+        L.moe_expert_ffn.restype = i32
+        L.moe_expert_ffn.argtypes = [D, p, p, p, p, p, p, p, sz, p]
+        L.moe_combine.restype = i32
+        L.moe_combine.argtypes = [D, p, p, p, p, p, p]
+        L.moe_layer_forward.restype = i32
+        L.moe_layer_forward.argtypes = [D, p, p, p, p, p, p, p, p, p, p, C.POINTER(MoeDebugOut), p,
+                                        sz, p]
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().moe_status_str(int(s)).decode()

@@ -1,0 +1,157 @@
+"""Thin torch-tensor binding of libmoe.so.
+
+Argument marshalling only: tensors become device pointers, the current HIP
+stream is passed along, status codes become exceptions.  Every step of the
+layer runs in the library's HIP kernels.  PyTorch provides device memory and
+streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import MoeDebugOut, MoeDims, MoeError
+
+_DT = {"bf16": _lib.MOE_BF16, "f32": _lib.MOE_F32}
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@dataclass(frozen=True)
+class Dims:
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    I_shared: int = 0
+    capacity: int = -1
+    renormalize: int = 1
+    dtype: str = "bf16"
+
+    def c(self) -> MoeDims:
+        return MoeDims(self.T, self.H, self.E, self.k, self.I, self.I_shared, self.capacity,
+                       self.renormalize, _DT[self.dtype])
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DT[self.dtype]
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(status, where):
+    if status != _lib.MOE_OK:
+        raise MoeError(status, where)
+
+
+def capacity(T: int, k: int, E: int, factor: float) -> int:
+    return int(_lib.lib().moe_capacity(T, k, E, factor))
+
+
+def workspace_bytes(d: Dims) -> int:
+    c = d.c()
+    return int(_lib.lib().moe_workspace_bytes(C.byref(c)))
+
+
+def workspace(d: Dims, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(d)
+    if n == 0:
+        raise ValueError(f"invalid dims {d}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gate(d: Dims, x, wg, logits, stream=None):
+    c = d.c()
+    _check(_lib.lib().moe_gate(C.byref(c), _ptr(x, d.torch_dtype, "x"),
+                               _ptr(wg, d.torch_dtype, "wg"),
+                               _ptr(logits, torch.float32, "logits"), _stream(stream)), "moe_gate")
+
+
+def route(d: Dims, logits, bias, ids, w, counts=None, dropped=None, n_dropped=None, ws=None,
+          stream=None):
+    c = d.c()
+    _check(_lib.lib().moe_route(
+        C.byref(c), _ptr(logits, torch.float32, "logits"), _ptr(bias, torch.float32, "bias"),
+        _ptr(ids, torch.int32, "ids"), _ptr(w, torch.float32, "w"),
+        _ptr(counts, torch.int32, "counts"), _ptr(dropped, torch.uint8, "dropped"),
+        _ptr(n_dropped, torch.int32, "n_dropped"), _ptr(ws, torch.uint8, "ws"),
+        0 if ws is None else ws.numel(), _stream(stream)), "moe_route")
+
+
+def permute(d: Dims, x, ids, dropped, offsets, row_token, pos, x_packed, ws, stream=None):
+    c = d.c()
+    _check(_lib.lib().moe_permute(
+        C.byref(c), _ptr(x, d.torch_dtype, "x"), _ptr(ids, torch.int32, "ids"),
+        _ptr(dropped, torch.uint8, "dropped"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(row_token, torch.int32, "row_token"), _ptr(pos, torch.int32, "pos"),
+        _ptr(x_packed, d.torch_dtype, "x_packed"), _ptr(ws, torch.uint8, "ws"),
+        0 if ws is None else ws.numel(), _stream(stream)), "moe_permute")
+
+
+def expert_ffn(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None):
+    c = d.c()
+    dt = d.torch_dtype
+    _check(_lib.lib().moe_expert_ffn(
+        C.byref(c), _ptr(x_packed, dt, "x_packed"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(w1, dt, "w1"), _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), _ptr(y_packed, dt, "y_packed"),
+        _ptr(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)),
+        "moe_expert_ffn")
+
+
+def combine(d: Dims, y_packed, pos, w, y_shared, y, stream=None):
+    c = d.c()
+    dt = d.torch_dtype
+    _check(_lib.lib().moe_combine(
+        C.byref(c), _ptr(y_packed, dt, "y_packed"), _ptr(pos, torch.int32, "pos"),
+        _ptr(w, torch.float32, "w"), _ptr(y_shared, dt, "y_shared"), _ptr(y, dt, "y"),
+        _stream(stream)), "moe_combine")
+
+
+def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None, debug=None,
+                  stream=None):
+    """The fused layer.  shared = (ws1, ws3, ws2) or None; debug: dict of tensors to fill
+    (keys: logits, topk_ids, topk_w, counts, offsets, pos, n_dropped).  Returns y."""
+    dt = d.torch_dtype
+    if y is None:
+        y = torch.empty((d.T, d.H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(d, x.device)
+    s1 = s3 = s2 = None
+    if shared is not None:
+        s1, s3, s2 = shared
+    dbg = None
+    if debug:
+        types = dict(logits=torch.float32, topk_ids=torch.int32, topk_w=torch.float32,
+                     counts=torch.int32, offsets=torch.int32, pos=torch.int32,
+                     n_dropped=torch.int32)
+        dbg = MoeDebugOut(**{k: _ptr(v, types[k], k) for k, v in debug.items() if k != "events"})
+        for i, ev in enumerate(debug.get("events") or []):
+            dbg.events[i] = ev  # raw hipEvent_t handles (or None)
+    c = d.c()
+    _check(_lib.lib().moe_layer_forward(
+        C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),
+        _ptr(w1, dt, "w1"), _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), _ptr(s1, dt, "ws1"),
+        _ptr(s3, dt, "ws3"), _ptr(s2, dt, "ws2"), _ptr(y, dt, "y"),
+        C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_layer_forward")
+    return y

@@ -1,0 +1,425 @@
+// C ABI of libmoe.so (declared in include/moe.h): argument checks, workspace
+// carving and the launch sequence of each call.  All compute is in the kernels
+// of route.hip, permute.hip, gemm_bf16.hip, gemm_f32.hip and combine.hip.
+#include "../../include/moe.h"
+#include "common.hpp"
+
+#include <limits.h>
+#include <math.h>
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Byte layout of the workspace; one layout serves every call.
+struct Layout {
+  size_t logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn, pos,
+      dropped, row_token, act, yp, yps, total;
+};
+
+int elem_bytes(const moe_dims_t* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
+
+Layout layout(const moe_dims_t* d) {
+  const size_t T = d->T, E = d->E, n = (size_t)d->T * d->k, es = elem_bytes(d);
+  const size_t ntiles = (n + kSlotTile - 1) / kSlotTile;
+  const bool fold = d->I_shared > 0 && d->I_shared == d->I;  // shared expert as one more group
+  const size_t rows = n + (fold ? T : 0);
+  const size_t imax = d->I_shared > d->I ? d->I_shared : d->I;
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes ? bytes : 1);
+    return at;
+  };
+  L.logits = take(T * E * 4);
+  L.ids = take(n * 4);
+  L.w = take(n * 4);
+  L.tile_hist = take(E * ntiles * 4);
+  L.tile_base = take(E * ntiles * 4);
+  L.raw = take(E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 2) * 4);
+  L.n_dropped = take(4);
+  L.ts_gu = take((E + 2) * 4);
+  L.ts_dn = take((E + 2) * 4);
+  L.pos = take(n * 4);
+  L.dropped = take(n);
+  L.row_token = take((n + T) * 4);
+  L.act = take(((rows > T ? rows : T)) * imax * es);
+  L.yp = take(rows * (size_t)d->H * es);
+  L.yps = take(d->I_shared > 0 && !fold ? T * (size_t)d->H * es : 0);
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return (P*)((char*)ws + off);
+}
+
+moe_status_t check_dims(const moe_dims_t* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->H <= 0 || d->E <= 0 || d->I <= 0 || d->I_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (d->k < 1 || d->k > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (d->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d->T * d->k > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_BF16) {
+    if (d->H % 64 || d->I % 64 || d->I_shared % 64) return MOE_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets of the MFMA path
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t n = (int64_t)d->T * d->k + d->T;
+    const int64_t imax = d->I_shared > d->I ? d->I_shared : d->I;
+    if ((int64_t)d->T * d->H * 2 >= lim || n * d->H * 2 >= lim || n * imax * 2 >= lim ||
+        (int64_t)imax * d->H * 2 >= lim || (int64_t)d->E * d->H * 2 >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (d->H % 4) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// record event i of the debug struct, when the caller asked for it
+hipError_t mark(void* const* ev, int i, hipStream_t s) {
+  if (!ev || !ev[i]) return hipSuccess;
+  return hipEventRecord((hipEvent_t)ev[i], s);
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                             \
+  do {                                            \
+    hipError_t _e = (expr);                       \
+    if (_e != hipSuccess) return MOE_ERR_HIP;     \
+  } while (0)
+
+// ---- step implementations shared by the step-wise and fused calls --------------------------
+
+hipError_t run_gate(const moe_dims_t* d, const void* x, const void* wg, float* logits,
+                    hipStream_t s) {
+  GroupedGemm p = {};
+  p.a = x;
+  p.a_rows = d->T;
+  p.max_rows = d->T;
+  p.b = wg;
+  p.N = d->E;
+  p.K = d->H;
+  p.c = logits;
+  p.ldc = d->E;
+  p.G = 1;
+  p.G_routed = 1;
+  p.static_rows = d->T;
+  if (d->dtype == MOE_BF16) return launch_gemm_bf16(GEMM_GATE, p, d->T, num_cus(), s);
+  int bm, nt;
+  gemm_f32_tiling(d->E, &bm, &nt);
+  return launch_gemm_f32(GEMM_GATE, p, ceil_div(d->T, bm) * nt, s);
+}
+
+PermuteArgs permute_args(const moe_dims_t* d, const Layout& L, void* ws) {
+  PermuteArgs a = {};
+  a.n = d->T * d->k;
+  a.k = d->k;
+  a.E = d->E;
+  a.T = d->T;
+  a.capacity = -1;
+  a.ntiles = ceil_div(a.n, kSlotTile);
+  a.tile_hist = at<int32_t>(ws, L.tile_hist);
+  a.tile_base = at<int32_t>(ws, L.tile_base);
+  a.raw = at<int32_t>(ws, L.raw);
+  a.counts = at<int32_t>(ws, L.counts);
+  a.offsets = at<int32_t>(ws, L.offsets);
+  a.n_dropped = at<int32_t>(ws, L.n_dropped);
+  return a;
+}
+
+// grouped gate-up + down over G groups whose packed row ranges are offsets[0..G]
+hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row_map,
+                   int64_t a_rows, int64_t max_rows, const int32_t* offsets, int G, int G_routed,
+                   const void* w1, const void* w3, const void* w2, const void* e1,
+                   const void* e3, const void* e2, void* act, void* out, int32_t* ts_gu,
+                   int32_t* ts_dn, int avg_rows, hipStream_t s, void* const* ev = nullptr) {
+  const bool bf16 = d->dtype == MOE_BF16;
+  int bm_gu, nt_gu, bm_dn, nt_dn;
+  if (bf16) {
+    gemm_bf16_tiling(GEMM_GATE_UP, avg_rows, I, &bm_gu, &nt_gu);
+    gemm_bf16_tiling(GEMM_DOWN, avg_rows, d->H, &bm_dn, &nt_dn);
+  } else {
+    gemm_f32_tiling(I, &bm_gu, &nt_gu);
+    gemm_f32_tiling(d->H, &bm_dn, &nt_dn);
+  }
+  hipError_t e = launch_tile_map(offsets, G, bm_gu, nt_gu, ts_gu, bm_dn, nt_dn, ts_dn, s);
+  if (e != hipSuccess) return e;
+  if ((e = mark(ev, MOE_EV_PERMUTE, s)) != hipSuccess) return e;
+
+  GroupedGemm gu = {};
+  gu.a = a;
+  gu.row_map = row_map;
+  gu.a_rows = a_rows;
+  gu.max_rows = max_rows;
+  gu.b = w1;
+  gu.b2 = w3;
+  gu.b_stride = (int64_t)I * d->H;
+  gu.b_extra = e1;
+  gu.b2_extra = e3;
+  gu.N = I;
+  gu.K = d->H;
+  gu.c = act;
+  gu.ldc = I;
+  gu.offsets = offsets;
+  gu.G = G;
+  gu.G_routed = G_routed;
+  gu.tile_start = ts_gu;
+
+  GroupedGemm dn = {};
+  dn.a = act;
+  dn.a_rows = max_rows;
+  dn.max_rows = max_rows;
+  dn.b = w2;
+  dn.b_stride = (int64_t)d->H * I;
+  dn.b_extra = e2;
+  dn.N = d->H;
+  dn.K = I;
+  dn.c = out;
+  dn.ldc = d->H;
+  dn.offsets = offsets;
+  dn.G = G;
+  dn.G_routed = G_routed;
+  dn.tile_start = ts_dn;
+
+  const int cus = num_cus();
+  const int64_t mt_gu = (ceil_div64(max_rows, bm_gu) + G) * nt_gu;
+  const int64_t mt_dn = (ceil_div64(max_rows, bm_dn) + G) * nt_dn;
+  e = bf16 ? launch_gemm_bf16(GEMM_GATE_UP, gu, avg_rows, cus, s)
+           : launch_gemm_f32(GEMM_GATE_UP, gu, (int)mt_gu, s);
+  if (e != hipSuccess) return e;
+  if ((e = mark(ev, MOE_EV_GATE_UP, s)) != hipSuccess) return e;
+  e = bf16 ? launch_gemm_bf16(GEMM_DOWN, dn, avg_rows, cus, s)
+           : launch_gemm_f32(GEMM_DOWN, dn, (int)mt_dn, s);
+  if (e != hipSuccess) return e;
+  return mark(ev, MOE_EV_DOWN, s);
+}
+
+// device offsets [0, T] of a single group covering every token
+__global__ void whole_range_kernel(int32_t* offsets, int T) {
+  offsets[0] = 0;
+  offsets[1] = T;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int32_t moe_capacity(int32_t T, int32_t k, int32_t E, double factor) {
+  if (E <= 0 || T < 0 || k < 0 || !(factor >= 0.0)) return -1;
+  return (int32_t)floor((double)T * (double)k / (double)E * factor);
+}
+
+size_t moe_workspace_bytes(const moe_dims_t* d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  return layout(d).total;
+}
+
+moe_status_t moe_gate(const moe_dims_t* d, const void* x, const void* wg, float* logits,
+                      void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !wg || !logits) return MOE_ERR_INVALID_ARG;
+  return hip_status(run_gate(d, x, wg, logits, (hipStream_t)stream));
+}
+
+moe_status_t moe_route(const moe_dims_t* d, const float* logits, const float* bias,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, uint8_t* dropped,
+                       int32_t* n_dropped, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_w) {
+    if (d->T > 0) return MOE_ERR_INVALID_ARG;
+  }
+  const bool need_ws = counts || dropped || n_dropped;
+  const Layout L = layout(d);
+  if (need_ws && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->T > 0)
+    MOE_TRY(launch_route(logits, bias, d->T, d->E, d->k, d->renormalize, topk_ids, topk_w, s));
+  if (!need_ws) return MOE_OK;
+  PermuteArgs a = permute_args(d, L, ws);
+  a.ids = topk_ids;
+  a.capacity = d->capacity;
+  if (counts) a.counts = counts;
+  if (n_dropped) a.n_dropped = n_dropped;
+  a.dropped = dropped;
+  MOE_TRY(launch_permute(a, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_permute(const moe_dims_t* d, const void* x, const int32_t* topk_ids,
+                         const uint8_t* dropped, int32_t* offsets, int32_t* row_token,
+                         int32_t* pos, void* x_packed, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!topk_ids || !row_token || !pos)) return MOE_ERR_INVALID_ARG;
+  if (x_packed && !x) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  PermuteArgs a = permute_args(d, L, ws);
+  a.ids = topk_ids;
+  a.inactive = dropped;
+  a.offsets = offsets;
+  a.pos = pos;
+  a.row_token = row_token;
+  MOE_TRY(launch_permute(a, s));
+  if (x_packed)
+    MOE_TRY(launch_pack_rows(x, row_token, offsets + d->E, d->T * d->k, d->H, elem_bytes(d),
+                             x_packed, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_dims_t* d, const void* x_packed, const int32_t* offsets,
+                            const void* w1, const void* w3, const void* w2, void* y_packed,
+                            void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!offsets || !w1 || !w3 || !w2) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!x_packed || !y_packed)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  const int64_t n = (int64_t)d->T * d->k;
+  const int avg = (int)(n / d->E);
+  MOE_TRY(run_ffn(d, d->I, x_packed, nullptr, n, n, offsets, d->E, d->E, w1, w3, w2, nullptr,
+                  nullptr, nullptr, at<void>(ws, L.act), y_packed, at<int32_t>(ws, L.ts_gu),
+                  at<int32_t>(ws, L.ts_dn), avg, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_dims_t* d, const void* y_packed, const int32_t* pos,
+                         const float* topk_w, const void* y_shared, void* y, void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!y_packed || !pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_combine(y_packed, pos, topk_w, y_shared, nullptr, d->T, d->H, d->k,
+                         d->dtype == MOE_BF16, y, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* wg,
+                               const float* bias, const void* w1, const void* w3, const void* w2,
+                               const void* ws1, const void* ws3, const void* ws2, void* y,
+                               const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                               void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!x || !wg || !w1 || !w3 || !w2 || !y) {
+    if (d->T > 0) return MOE_ERR_INVALID_ARG;
+  }
+  if (d->I_shared > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = d->T, E = d->E, k = d->k, n = T * k;
+  const bool shared = d->I_shared > 0;
+  const bool fold = shared && d->I_shared == d->I;
+
+  float* logits = dbg && dbg->logits ? dbg->logits : at<float>(ws, L.logits);
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* w = at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+
+  void* const* ev = dbg ? dbg->events : nullptr;
+  // 1. gate  2. softmax / top-k / renormalise
+  MOE_TRY(mark(ev, MOE_EV_START, s));
+  MOE_TRY(run_gate(d, x, wg, logits, s));
+  MOE_TRY(mark(ev, MOE_EV_GATE, s));
+  MOE_TRY(launch_route(logits, bias, T, E, k, d->renormalize, ids, w, s));
+  MOE_TRY(mark(ev, MOE_EV_ROUTE, s));
+  // 3. count, capacity, scan, stable scatter (rows of the folded shared expert appended)
+  PermuteArgs a = permute_args(d, L, ws);
+  a.ids = ids;
+  a.capacity = d->capacity;
+  a.shared_rows = fold ? T : 0;
+  a.dropped = at<uint8_t>(ws, L.dropped);
+  a.pos = pos;
+  a.row_token = row_token;
+  MOE_TRY(launch_permute(a, s));
+  // 4-5. grouped gate-up (rows gathered straight from x) and down
+  const int G = E + (fold ? 1 : 0);
+  const int64_t max_rows = (int64_t)n + (fold ? T : 0);
+  const int avg = n / E;
+  void* yp = at<void>(ws, L.yp);
+  MOE_TRY(run_ffn(d, d->I, x, row_token, T, max_rows, offsets, G, E, w1, w3, w2,
+                  fold ? ws1 : nullptr, fold ? ws3 : nullptr, fold ? ws2 : nullptr,
+                  at<void>(ws, L.act), yp, at<int32_t>(ws, L.ts_gu), at<int32_t>(ws, L.ts_dn), avg,
+                  s, ev));
+  const void* ys = nullptr;
+  const int32_t* ys_row0 = nullptr;
+  if (fold) {
+    ys = yp;
+    ys_row0 = offsets + E;  // the shared rows start after the R routed rows
+  } else if (shared) {
+    // a shared expert of another inner size runs as its own single-group FFN over x; the
+    // tile maps, the activation buffer and `raw` (free once the permute has run) are reused
+    // in stream order
+    int32_t* off2 = at<int32_t>(ws, L.raw);  // two ints: [0, T]
+    whole_range_kernel<<<1, 1, 0, s>>>(off2, T);
+    MOE_TRY(hipGetLastError());
+    MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 0, ws1, ws3, ws2, nullptr, nullptr,
+                    nullptr, at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
+                    at<int32_t>(ws, L.ts_dn), T, s));
+    ys = at<void>(ws, L.yps);
+  }
+  // 6. weighted combine back into token order
+  MOE_TRY(launch_combine(yp, pos, w, ys, ys_row0, T, d->H, k, d->dtype == MOE_BF16, y, s));
+  MOE_TRY(mark(ev, MOE_EV_END, s));
+
+  if (dbg) {
+    if (dbg->topk_ids)
+      MOE_TRY(hipMemcpyAsync(dbg->topk_ids, ids, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->topk_w)
+      MOE_TRY(hipMemcpyAsync(dbg->topk_w, w, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->counts)
+      MOE_TRY(hipMemcpyAsync(dbg->counts, at<int32_t>(ws, L.counts), (size_t)E * 4,
+                             hipMemcpyDeviceToDevice, s));
+    if (dbg->offsets)
+      MOE_TRY(hipMemcpyAsync(dbg->offsets, offsets, (size_t)(E + 1) * 4, hipMemcpyDeviceToDevice,
+                             s));
+    if (dbg->pos) MOE_TRY(hipMemcpyAsync(dbg->pos, pos, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->n_dropped)
+      MOE_TRY(hipMemcpyAsync(dbg->n_dropped, at<int32_t>(ws, L.n_dropped), 4,
+                             hipMemcpyDeviceToDevice, s));
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations shared by the HIP sources of libmoe.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kSlotTile = 1024;    // routing slots handled by one permute block
+constexpr int kMaxExperts = 1024;  // routed experts the routing kernels support
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns hipGetLastError() of its launch(es)).
+// ---------------------------------------------------------------------------
+
+// route.hip: one wavefront per token; softmax, top-k, renormalise.
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
+                        int renormalize, int32_t* ids, float* w, hipStream_t s);
+
+// permute.hip
+struct PermuteArgs {
+  const int32_t* ids;      // [n] expert of each slot (slot = t*k + j)
+  const uint8_t* inactive; // [n] or null: 1 = slot takes no part (already dropped)
+  int n, k, E, T;
+  int capacity;            // < 0 unlimited
+  int ntiles;              // ceil(n / kSlotTile)
+  int32_t* tile_hist;      // [E * ntiles]
+  int32_t* tile_base;      // [E * ntiles]
+  int32_t* raw;            // [E]
+  int32_t* counts;         // [E]   kept
+  int32_t* offsets;        // [E+2] (E+1 used when shared_rows > 0)
+  int32_t* n_dropped;      // [1]
+  int shared_rows;         // T when the always-on expert follows the routed rows, else 0
+  // outputs of the rank pass (any may be null)
+  uint8_t* dropped;        // [n]
+  int32_t* pos;            // [n]
+  int32_t* row_token;      // [n + shared_rows]
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+hipError_t launch_pack_rows(const void* x, const int32_t* row_token, const int32_t* n_rows,
+                            int max_rows, int H, int elem_bytes, void* xp, hipStream_t s);
+
+// tile map of the grouped GEMMs: tile_start[g] = sum over g' < g of ceil(rows_g' / bm) * nt
+hipError_t launch_tile_map(const int32_t* offsets, int G, int bm0, int nt0, int32_t* start0,
+                           int bm1, int nt1, int32_t* start1, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* yp, const int32_t* pos, const float* w, const void* ys,
+                          const int32_t* ys_row0, int T, int H, int k, int bf16, void* y,
+                          hipStream_t s);
+
+// gemm_bf16.hip / gemm_f32.hip: grouped GEMMs
+enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
+
+struct GroupedGemm {
+  // A: packed rows [*, K]; row r of group g reads A row (row_map ? row_map[r] : r)
+  const void* a;
+  const int32_t* row_map;
+  int64_t a_rows;            // rows addressable in a (for range checks)
+  int64_t max_rows;          // upper bound of the packed rows over all groups
+  // B: per group [N_b, K] with N_b = N (or 2 panels of N for SwiGLU: b and b2)
+  const void* b;             // routed group g uses b + g * b_stride
+  const void* b2;            // SwiGLU second panel (W3), same strides
+  int64_t b_stride;          // elements between consecutive groups' matrices
+  const void* b_extra;       // the always-on group (index G_routed), or null
+  const void* b2_extra;
+  int N, K;                  // output columns, reduction length
+  // output C [*, ldc]
+  void* c;
+  int ldc;
+  // groups
+  const int32_t* offsets;    // [G+1] packed row range of each group (device) or null
+  int G;                     // groups (routed + extra)
+  int G_routed;
+  int static_rows;           // rows of the single group when offsets == null
+  const int32_t* tile_start; // [G+1] device tile map, or null with offsets == null
+};
+
+// bf16 MFMA paths
+enum GemmKind { GEMM_GATE = 0, GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
+// tiles per group needed by the chosen configuration
+void gemm_bf16_tiling(GemmKind kind, int max_rows_per_group, int N, int* bm, int* nt);
+hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& g, int max_rows_per_group,
+                            int num_cus, hipStream_t s);
+
+// fp32 vector-FMA paths
+void gemm_f32_tiling(int N, int* bm, int* nt);
+hipError_t launch_gemm_f32(GemmKind kind, const GroupedGemm& g, int max_tiles, hipStream_t s);
+
+}  // namespace moe

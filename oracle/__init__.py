@@ -31,6 +31,8 @@ def lib():
         if not os.path.exists(_build.LIB):
             _build.build()
         L = C.CDLL(_build.LIB)
+        L.oracle_threads.restype = C.c_int
+        L.oracle_threads.argtypes = []
         L.oracle_capacity.restype = _i32
         L.oracle_capacity.argtypes = [_i32, _i32, _i32, C.c_double]
         L.oracle_gate.restype = None
@@ -65,6 +67,10 @@ def _c(a, dtype=None):
     if a is None:
         return None
     return np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
 
 
 def capacity(T: int, k: int, E: int, factor: float | None) -> int:

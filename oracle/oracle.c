@@ -10,8 +10,11 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* exact float64 value of element i of a bf16 or fp32 tensor */
 static double ld(int dt, const void* p, int64_t i) {

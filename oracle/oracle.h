@@ -31,6 +31,9 @@
 extern "C" {
 #endif
 
+/* OpenMP threads the parallel outer loops use */
+int oracle_threads(void);
+
 /* storage type of a tensor argument */
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
 

@@ -1,0 +1,84 @@
+"""GPU parity of moe_route (softmax, top-k, renormalise, capacity drop) with the oracle.
+
+Both sides get the same fp32 logits, so ids, counts, drop flags and drop totals
+must be bit-exact; weights agree to 1e-6 absolute (fp32 exp on the GPU against
+float64 in the oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from gpu_util import dev, log, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+import mixture_experts_layer_scatter_amd as moe
+
+
+def _run(logits, k, bias=None, renorm=1, capacity=-1):
+    T, E = logits.shape
+    d = moe.Dims(T=T, H=64, E=E, k=k, I=64, capacity=capacity, renormalize=renorm)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    dropped = torch.empty((T, k), dtype=torch.uint8, device="cuda")
+    nd = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = moe.workspace(d)
+    moe.route(d, dev(logits), None if bias is None else dev(bias), ids, w, counts, dropped, nd, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), counts.cpu().numpy(), dropped.cpu().numpy(), int(nd.item())
+
+
+def _check(logits, k, bias=None, renorm=1, capacity=-1):
+    T, E = logits.shape
+    ids, w, counts, dropped, nd = _run(logits, k, bias, renorm, capacity)
+    oids, ow, _ = oracle.route(logits, k, bias=bias, renormalize=renorm)
+    assert np.array_equal(ids, oids), f"ids differ at {np.argwhere(ids != oids)[:5].tolist()}"
+    assert np.abs(w - ow).max() <= 1e-6
+    p = oracle.permute(oids, E, capacity)
+    assert np.array_equal(counts, p["counts"])
+    assert np.array_equal(dropped, p["dropped"])
+    assert nd == p["n_dropped"]
+    return p
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (3, 2), (5, 5), (8, 2), (64, 2), (128, 8), (256, 8),
+                                 (100, 100), (1024, 16), (1024, 1)])
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_route_bit_exact_with_ties(E, k, renorm):
+    need_gpu()
+    log(f"route E={E} k={k} renorm={renorm}")
+    for T in (1, 77, 2500):
+        logits = moe_synth.random_logits(seed=E * 7 + k, T=T, E=E, ties=True)
+        bias = None
+        if E % 2 == 0:
+            bias = np.random.default_rng(E).standard_normal(E).astype(np.float32)
+        _check(logits, k, bias, renorm)
+
+
+@pytest.mark.parametrize("cap", [0, 1, 3, 50, 10 ** 6])
+def test_capacity_drops_in_token_order(cap):
+    need_gpu()
+    rng = np.random.default_rng(cap)
+    T, E, k = 3000, 16, 2
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    logits[:, 3] += 2.0  # a hot expert
+    p = _check(logits, k, capacity=cap)
+    if cap == 10 ** 6:
+        assert p["n_dropped"] == 0
+
+
+@pytest.mark.parametrize("name", ["qwen3_prefill", "skewed_capacity", "dsv3_decode"])
+def test_route_full_size_on_oracle_logits(name):
+    need_gpu()
+    w = moe_synth.get(name)
+    log(f"route full size {name}: oracle gate on {w.T} tokens")
+    x = moe_synth.x(w)
+    logits = oracle.gate(x, moe_synth.gate_weight(w))
+    cap = oracle.capacity(w.T, w.k, w.E, w.capacity_factor)
+    p = _check(logits, w.k, moe_synth.logit_bias(w), w.renormalize, cap)
+    log(f"  kept {int(p['counts'].sum())} of {w.T * w.k}, dropped {p['n_dropped']}")
+    if name == "skewed_capacity":
+        assert cap == 640 and p["n_dropped"] > 0
