@@ -38,6 +38,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes three times "
+                         "(calibrates the HBM byte counters of a profiler); prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
@@ -46,6 +49,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe)
+        return
 
     import mixture_experts_layer_scatter_amd as moe
     from mixture_experts_layer_scatter_amd import _lib
@@ -126,6 +133,7 @@ def main():
         achieved = gu_flops / (gu_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = profiled_traffic(w.name)
     roof["kernel"] = "gemm_bf16_kernel (grouped gate-up + SiLU*mul)"
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
@@ -157,6 +165,53 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def kernel_source_digest():
+    """sha256 over the sources the grouped GEMM kernel is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_scatter_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload):
+    """HBM bytes per gate-up launch from the committed FETCH_SIZE/WRITE_SIZE counter summary.
+
+    The figure is reported only while the kernel sources still hash to the digest the
+    counters were taken with; otherwise it is stale and the result is None.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                key, _, val = line.partition(" ")
+                kv[key] = val.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    return float(kv["bytes_per_launch"])
+
+
+def copy_probe(nbytes):
+    """A plain copy of known size: reads and writes nbytes of HBM per launch."""
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)                 # runtime device-to-device copy
+    for _ in range(3):
+        torch.neg(src, out=dst)        # elementwise kernel with the same traffic
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies and 3 negations of {n * 4} bytes")
 
 
 def cpu_baseline(w, target_s):
