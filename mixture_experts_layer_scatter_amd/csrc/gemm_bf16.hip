@@ -8,15 +8,14 @@
 // W3 x)).  "MoE 推理架构深度实战：从 Expert Parallelism 到 DeepSeek-V3 的工程落地"
 // §2.1: the gate is a linear map from hidden size to experts without bias.
 //
-// Design for gfx950:
+// Design for gfx950 (two kernels share the conventions below):
 //  * C[r, n] = sum_k A[r, k] * B[n, k]; both operands are contiguous along k,
 //    so one 16-byte load gives an MFMA lane its 8 consecutive k values.
-//  * Block tile BM x BN, k-step 64, v_mfma_f32_32x32x16_bf16 with fp32
-//    accumulators; WM x WN wavefronts, each owning a (BM/WM) x (BN/WN) tile.
+//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulators, k-step 64.
 //  * Operand tiles go HBM -> LDS with buffer_load ... lds (16 bytes per lane,
-//    no VGPR staging), STAGES deep.  An LDS row holds 64 bf16 = eight 16-byte
-//    chunks; chunk c of row r is stored at chunk c ^ (r & 7), so the eight
-//    rows an MFMA fragment read touches fall in distinct banks.
+//    no VGPR staging).  An LDS row holds 64 bf16 = eight 16-byte chunks; chunk
+//    c of row r is stored at chunk c ^ swz(r), so the rows one MFMA fragment
+//    read touches fall in distinct banks.
 //  * Buffer loads return zero past the resource's size and for the
 //    out-of-range offset used for rows beyond a group: ragged row tails and
 //    column tails need no branches.
@@ -29,7 +28,23 @@
 //  * Gate-up: the B tile interleaves 32-row blocks of W1 and W3, so each
 //    wavefront holds W1 x and W3 x for the same columns in registers and
 //    applies silu(a) * g before one bf16 store of the activation.
+//
+// Prefill kernel (gemm_big_kernel, rows per group >= 128): 256 x 256 tiles,
+// 8 wavefronts (two per SIMD, each 128 token rows x 64 columns), two LDS
+// stages.  The weights are the MFMA's first operand, so each lane ends with 4
+// consecutive output columns of one token row and stores them straight from
+// registers; the next tile's first loads go out before that epilogue.  The
+// barrier inside the k-loop leaves the loads of the stage in flight alone
+// (s_barrier without a memory-counter drain).  A wavefront owns the token
+// blocks wm, wm+2, ... of its tile and skips the MFMAs of blocks past the
+// group's last row, so a ragged last row tile costs its rows, not 256.
+//
+// Small-group kernel (gemm_bf16_kernel, decode and the gate): 32-row tiles,
+// four wavefronts across the columns, four LDS stages to keep weight bytes in
+// flight; the activation tile is staged through LDS for 16-byte row stores.
 #include "common.hpp"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -42,8 +57,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                           int soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
 // wait until at most n vector-memory operations of this wavefront are outstanding
@@ -284,6 +300,299 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(GroupedGemm p)
   }
 }
 
+// ---- prefill kernel ----------------------------------------------------------------------------
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
+// vmcnt[5:4] bits 15:14); "no wait" is the field's maximum
+template <int n>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(n >= 0 && n < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xf | (0x3 << 14) | (0x7 << 4) | (n << 8));
+}
+
+// Workgroup barrier that leaves outstanding global->LDS loads in flight (the caller has waited
+// for exactly what it needs); also a compiler fence, so no LDS access moves across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// silu(a) = a * sigmoid(a) with the hardware exp2 and reciprocal (the result is rounded to bf16)
+__device__ __forceinline__ float silu_fast(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// swizzle of the 16-byte chunks of a 128-byte LDS row: distinct banks for the 8 (and the 16)
+// consecutive rows that one fragment read serves per cycle
+__device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+namespace big {
+constexpr int BM = 256, BN = 256, WM = 2, WN = 4, WAVES = WM * WN, THREADS = WAVES * kWave;
+constexpr int WTN = BN / WN;            // 64 columns per wavefront
+constexpr int TM = BM / WM / 32;        // 4 token blocks of 32 rows per wavefront
+constexpr int TN = WTN / 32;            // 2 column blocks of 32
+constexpr int KK = kBK / 16;            // MFMA k-steps per LDS stage
+constexpr int RPL = 1024 / kRowBytes;   // rows one 1 KB wavefront load covers
+constexpr int A_LOADS = BM / RPL / WAVES, B_LOADS = BN / RPL / WAVES, L = A_LOADS + B_LOADS;
+constexpr int A_BYTES = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
+constexpr int LDS = 2 * STAGE;          // two stages: 128 KB
+static_assert(A_LOADS * RPL * WAVES == BM && B_LOADS * RPL * WAVES == BN, "load split");
+static_assert(LDS <= 160 * 1024, "LDS budget");
+}  // namespace big
+
+template <int EPI, bool GATHER, int GN>
+__global__ __launch_bounds__(big::THREADS) void gemm_big_kernel(GroupedGemm p) {
+  using namespace big;
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_BF16, "bf16 outputs only");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wid / WN, wn = wid % WN;
+  const int K = p.K, KT = K / kBK;
+  const int total = p.tile_start[p.G];
+  const int nx = gridDim.x / 8, xcd = blockIdx.x % 8;
+  const int per_xcd = (total + 7) / 8;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * 2));
+
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int sw = row_swizzle(l32);
+  // wavefront row wm owns token blocks wm, wm + 2, wm + 4, wm + 6 of its tile
+  const uint32_t a_frag = (uint32_t)((wm * 32 + l32) * kRowBytes);
+  const uint32_t b_frag = (uint32_t)(A_BYTES + (wn * WTN + l32) * kRowBytes);
+
+  struct Tile {
+    int row_base, m0, rows_here, n_t, g;
+  };
+  auto locate = [&](int it, Tile& t) -> bool {
+    if (it >= per_xcd) return false;
+    const int tile = xcd * per_xcd + it;
+    if (tile >= total) return false;
+    int lo = 0, hi2 = p.G;  // largest g with tile_start[g] <= tile
+    while (hi2 - lo > 1) {
+      const int mid = (lo + hi2) >> 1;
+      if (p.tile_start[mid] <= tile) lo = mid;
+      else hi2 = mid;
+    }
+    const int g = lo, li = tile - p.tile_start[g];
+    const int row_base = p.offsets[g], rows = p.offsets[g + 1] - row_base;
+    const int mt = (rows + BM - 1) / BM;
+    const int nblk = li / (mt * GN), rem = li % (mt * GN);
+    t.g = g;
+    t.row_base = row_base;
+    t.m0 = (rem % mt) * BM;
+    t.n_t = nblk * GN + rem / mt;
+    t.rows_here = min(BM, rows - t.m0);
+    return true;
+  };
+
+  // per-lane source offsets of the current tile's loads (lane: row lane / 8, chunk lane % 8)
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+  __amdgpu_buffer_rsrc_t rB, rB2;
+  auto setup = [&](const Tile& t) {
+    const bool extra = t.g >= p.G_routed;
+    const char* bbase =
+        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.g * p.b_stride * 2);
+    const char* b2base = bbase;
+    if (EPI == EPI_SWIGLU)
+      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)t.g * p.b_stride * 2);
+    const uint32_t b_bytes = (uint32_t)((int64_t)p.N * K * 2);
+    rB = make_rsrc(bbase, b_bytes);
+    rB2 = make_rsrc(b2base, b_bytes);
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int r = (wid * A_LOADS + i) * RPL + lane / 8;
+      const int c = (lane & 7) ^ row_swizzle(r);
+      uint32_t off = kOutOfRange;
+      if (r < t.rows_here) {
+        const int prow = t.row_base + t.m0 + r;
+        const int64_t src = GATHER ? (int64_t)p.row_map[prow] : (int64_t)prow;
+        off = (uint32_t)(src * K * 2) + c * 16;
+      }
+      a_off[i] = off;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int n = (wid * B_LOADS + i) * RPL + lane / 8;
+      const int c = (lane & 7) ^ row_swizzle(n);
+      const int src = EPI == EPI_SWIGLU ? t.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.n_t * BN + n;
+      b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * 2u + c * 16 : kOutOfRange;
+    }
+  };
+  // stage kt into LDS slot `slot`; past the last stage every lane gets the out-of-range offset
+  // (no memory access, zeros into a free slot), so every step issues the same number of loads
+  auto issue = [&](int kt, int slot, bool valid) {
+    char* sa = smem + slot * STAGE;
+    char* sb = sa + A_BYTES;
+    const int kb = valid ? kt * kRowBytes : 0;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      load_lds16(rA, sa + (wid * A_LOADS + i) * 1024, valid ? a_off[i] : kOutOfRange, kb);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int blk = wid * B_LOADS + i;
+      const bool second = EPI == EPI_SWIGLU && (((blk * RPL) >> 5) & 1);
+      load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kb);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+  bf16x8 fa[2][TM], fb[2][TN];
+
+  // The k-loop with NB active token blocks for this wavefront.  Every NB runs the same loads,
+  // waits and barriers, so the wavefronts of the block stay in step.  At the barrier in the
+  // middle of step kt every wavefront has read all of stage kt, whose slot then takes stage
+  // kt + 2 while the last MFMAs of step kt run from registers.
+  auto kloop = [&](auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    auto read_frags = [&](const char* st, int kk, int buf) {
+      const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 64 * kRowBytes);
+      if (NB > 0) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + coff + j * 32 * kRowBytes);
+      }
+    };
+    // weights as the first operand: D[column][token]
+    auto mfmas = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    };
+    read_frags(smem, 0, 0);
+    if (1 < KT) issue(1, 1, true);
+    for (int kt = 0; kt < KT; ++kt) {
+      const char* cur = smem + (kt & 1) * STAGE;
+      const char* nxt = smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk < KK - 1) {
+          read_frags(cur, kk + 1, (kk + 1) & 1);
+        } else {
+          wait_vmcnt<0>();       // stage kt + 1 landed (this wavefront's share)
+          wait_lgkmcnt<0>();     // this wavefront's reads of stage kt returned
+          barrier_keep_loads();  // ... and everyone else's
+          read_frags(nxt, 0, 0);
+          issue(kt + 2, kt & 1, kt + 2 < KT);
+        }
+        mfmas(kk & 1);
+        // interleave: one MFMA, then one LDS read and (after the barrier) one global load
+#pragma unroll
+        for (int m = 0; m < NB * TN; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (m < NB + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (kk == KK - 1 && m < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+    }
+  };
+
+  int it = blockIdx.x / 8;
+  Tile cur;
+  if (!locate(it, cur)) return;
+  setup(cur);
+  issue(0, 0, true);
+
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    wait_vmcnt<0>();  // stage 0 (and the previous tile's stores)
+    barrier_keep_loads();
+    const int nblocks = (cur.rows_here + 31) >> 5;
+    const int nb = (nblocks - wm + 1) >> 1;  // active token blocks of this wavefront
+    switch (nb) {
+      case 4: kloop(std::integral_constant<int, 4>()); break;
+      case 3: kloop(std::integral_constant<int, 3>()); break;
+      case 2: kloop(std::integral_constant<int, 2>()); break;
+      case 1: kloop(std::integral_constant<int, 1>()); break;
+      default: kloop(std::integral_constant<int, 0>()); break;
+    }
+    // everyone is done with the operand slots and the loads past the last stage have landed
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier_keep_loads();
+
+    const Tile done = cur;
+    const int done_nb = nb;
+    it += nx;
+    const bool more = locate(it, cur);
+    if (more) {  // the next tile's first stage loads while this tile's results go out
+      setup(cur);
+      issue(0, 0, true);
+    }
+
+    // epilogue: lane holds token l32 of block (2i + wm) and columns 8q + 4hi + (0..3) of
+    // each 32-column block j
+    const int64_t out_row0 = (int64_t)done.row_base + done.m0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= done_nb) break;
+      const int tok = (2 * i + wm) * 32 + l32;
+      if (tok >= done.rows_here) continue;
+      uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // blocks j (W1) and j + 1 (W3) hold the same 32 columns
+#pragma unroll
+        for (int j = 0; j < TN; j += 2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = done.n_t * (BN / 2) + wn * (WTN / 2) + (j / 2) * 32 + 8 * q + 4 * hi;
+            if (col < p.N) {
+              float h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) h[e] = silu_fast(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
+              uint2 v;
+              v.x = pack_bf16x2(h[0], h[1]);
+              v.y = pack_bf16x2(h[2], h[3]);
+              *(uint2*)(crow + col) = v;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = done.n_t * BN + wn * WTN + j * 32 + 8 * q + 4 * hi;
+            if (col < p.N) {
+              uint2 v;
+              v.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+              v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              *(uint2*)(crow + col) = v;
+            }
+          }
+      }
+    }
+    if (!more) break;
+  }
+}
+
+template <int EPI, bool GATHER>
+static hipError_t run_big(const GroupedGemm& p, int max_tiles, int num_cus, hipStream_t s) {
+  auto kern = gemm_big_kernel<EPI, GATHER, 8>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS);
+  if (e != hipSuccess) return e;
+  if (max_tiles <= 0) return hipSuccess;
+  int grid = num_cus;  // one workgroup (8 wavefronts, 128 KB of LDS) per CU
+  if (grid > max_tiles) grid = max_tiles;
+  grid = (grid + 7) / 8 * 8;
+  kern<<<grid, big::THREADS, big::LDS, s>>>(p);
+  return hipGetLastError();
+}
+
 // ---- configurations ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int STAGES, int EPI, bool GATHER, int GN>
 static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStream_t s) {
@@ -336,15 +645,16 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
     return run<32, 256, 1, 4, 4, EPI_F32, false, 1>(p, mt, num_cus, s);
   }
   const bool big = bm == 256;
+  if (big && !p.tile_start) return hipErrorInvalidValue;  // the prefill kernel walks a tile map
   if (kind == GEMM_GATE_UP) {
     const bool gather = p.row_map != nullptr;
     if (big)
-      return gather ? run<256, 256, 2, 2, 2, EPI_SWIGLU, true, 8>(p, mt, num_cus, s)
-                    : run<256, 256, 2, 2, 2, EPI_SWIGLU, false, 8>(p, mt, num_cus, s);
+      return gather ? run_big<EPI_SWIGLU, true>(p, mt, num_cus, s)
+                    : run_big<EPI_SWIGLU, false>(p, mt, num_cus, s);
     return gather ? run<32, 256, 1, 4, 4, EPI_SWIGLU, true, 1>(p, mt, num_cus, s)
                   : run<32, 256, 1, 4, 4, EPI_SWIGLU, false, 1>(p, mt, num_cus, s);
   }
-  if (big) return run<256, 256, 2, 2, 2, EPI_BF16, false, 8>(p, mt, num_cus, s);
+  if (big) return run_big<EPI_BF16, false>(p, mt, num_cus, s);
   return run<32, 256, 1, 4, 4, EPI_BF16, false, 1>(p, mt, num_cus, s);
 }
 
