@@ -17,11 +17,23 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Byte layout of the workspace; one layout serves every call.
 struct Layout {
-  size_t logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn, pos,
+  size_t gate_part, logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn, pos,
       dropped, row_token, act, yp, yps, total;
 };
 
 int elem_bytes(const moe_dims_t* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
+
+// Split-K factor of the fused layer's bf16 gate: enough workgroups to fill the GPU when there
+// are few (token, expert) tiles, keeping at least 4 k-steps per split.
+int gate_splits(const moe_dims_t* d) {
+  if (d->dtype != MOE_BF16 || d->T <= 0) return 1;
+  const int bn = d->E <= 32 ? 32 : d->E <= 64 ? 64 : d->E <= 128 ? 128 : 256;
+  const int64_t tiles = (int64_t)ceil_div(d->T, 32) * ceil_div(d->E, bn);
+  const int kt = d->H / 64;
+  int s = 1;
+  while (s < 16 && tiles * s * 2 <= 1024 && kt / (s * 2) >= 4) s *= 2;
+  return s;
+}
 
 Layout layout(const moe_dims_t* d) {
   const size_t T = d->T, E = d->E, n = (size_t)d->T * d->k, es = elem_bytes(d);
@@ -36,6 +48,8 @@ Layout layout(const moe_dims_t* d) {
     o += align_up(bytes ? bytes : 1);
     return at;
   };
+  const int gs = gate_splits(d);
+  L.gate_part = take(gs > 1 ? (size_t)gs * T * E * 4 : 0);
   L.logits = take(T * E * 4);
   L.ids = take(n * 4);
   L.w = take(n * 4);
@@ -109,8 +123,9 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 
 // ---- step implementations shared by the step-wise and fused calls --------------------------
 
+// splits > 1 needs `part` with room for splits * T * E floats
 hipError_t run_gate(const moe_dims_t* d, const void* x, const void* wg, float* logits,
-                    hipStream_t s) {
+                    hipStream_t s, int splits = 1, float* part = nullptr) {
   GroupedGemm p = {};
   p.a = x;
   p.a_rows = d->T;
@@ -123,7 +138,15 @@ hipError_t run_gate(const moe_dims_t* d, const void* x, const void* wg, float* l
   p.G = 1;
   p.G_routed = 1;
   p.static_rows = d->T;
-  if (d->dtype == MOE_BF16) return launch_gemm_bf16(GEMM_GATE, p, d->T, num_cus(), s);
+  if (d->dtype == MOE_BF16) {
+    if (splits <= 1 || !part) return launch_gemm_bf16(GEMM_GATE, p, d->T, num_cus(), s);
+    p.c = part;
+    p.ksplit = splits;
+    p.c_split_stride = (int64_t)d->T * d->E;
+    hipError_t e = launch_gemm_bf16(GEMM_GATE, p, d->T, num_cus(), s);
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce(part, splits, (int64_t)d->T * d->E, logits, s);
+  }
   int bm, nt;
   gemm_f32_tiling(d->E, &bm, &nt);
   return launch_gemm_f32(GEMM_GATE, p, ceil_div(d->T, bm) * nt, s);
@@ -360,7 +383,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
   void* const* ev = dbg ? dbg->events : nullptr;
   // 1. gate  2. softmax / top-k / renormalise
   MOE_TRY(mark(ev, MOE_EV_START, s));
-  MOE_TRY(run_gate(d, x, wg, logits, s));
+  MOE_TRY(run_gate(d, x, wg, logits, s, gate_splits(d), at<float>(ws, L.gate_part)));
   MOE_TRY(mark(ev, MOE_EV_GATE, s));
   MOE_TRY(launch_route(logits, bias, T, E, k, d->renormalize, ids, w, s));
   MOE_TRY(mark(ev, MOE_EV_ROUTE, s));

@@ -96,6 +96,8 @@ struct GroupedGemm {
   int G_routed;
   int static_rows;           // rows of the single group when offsets == null
   const int32_t* tile_start; // [G+1] device tile map, or null with offsets == null
+  int ksplit;                // > 1: split the reduction (fp32 output only), partial s at
+  int64_t c_split_stride;    //      c + s * c_split_stride (elements)
 };
 
 // bf16 MFMA paths
@@ -104,6 +106,9 @@ enum GemmKind { GEMM_GATE = 0, GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
 void gemm_bf16_tiling(GemmKind kind, int max_rows_per_group, int N, int* bm, int* nt);
 hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& g, int max_rows_per_group,
                             int num_cus, hipStream_t s);
+
+// out[i] = sum_s part[s * n + i] (fixed order)
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out, hipStream_t s);
 
 // fp32 vector-FMA paths
 void gemm_f32_tiling(int N, int* bm, int* nt);

@@ -69,6 +69,37 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
+// vmcnt[5:4] bits 15:14); "no wait" is the field's maximum
+template <int n>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(n >= 0 && n < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xf | (0x3 << 14) | (0x7 << 4) | (n << 8));
+}
+
+// Workgroup barrier that leaves outstanding global->LDS loads in flight (the caller has waited
+// for exactly what it needs); also a compiler fence, so no LDS access moves across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// silu(a) = a * sigmoid(a) with the hardware exp2 and reciprocal (the result is rounded to bf16)
+__device__ __forceinline__ float silu_fast(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// swizzle of the 16-byte chunks of a 128-byte LDS row: distinct banks for the 8 (and the 16)
+// consecutive rows that one fragment read serves per cycle
+__device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -111,17 +142,24 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(GroupedGemm p)
   const int K = p.K, KT = K / kBK;
   const int NT = (EPI == EPI_SWIGLU) ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
 
-  int total;
-  if (p.tile_start) total = p.tile_start[p.G];
-  else total = (p.static_rows + BM - 1) / BM * NT;
+  int total_base;
+  if (p.tile_start) total_base = p.tile_start[p.G];
+  else total_base = (p.static_rows + BM - 1) / BM * NT;
+  // split-K: ksplit consecutive copies of the tile list, copy ks reducing over its share of
+  // the k-steps into the partial output c + ks * c_split_stride
+  const int ks_n = p.ksplit > 1 ? p.ksplit : 1;
+  const int total = total_base * ks_n;
   const int nx = gridDim.x / 8, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per_xcd = (total + 7) / 8;
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * 2));
 
   for (int it = slot; it < per_xcd; it += nx) {
-    const int tile = xcd * per_xcd + it;
-    if (tile >= total) break;
+    const int tile_all = xcd * per_xcd + it;
+    if (tile_all >= total) break;
+    const int ks = tile_all / total_base, tile = tile_all - ks * total_base;
+    const int kt0 = (int)((int64_t)ks * KT / ks_n), kt1 = (int)((int64_t)(ks + 1) * KT / ks_n);
+    const int KTL = kt1 - kt0;  // k-steps of this tile
     // ---- locate the tile: group, row tile, column tile -----------------------------------
     int g = 0, row_base = 0, rows = p.static_rows, li = tile;
     if (p.tile_start) {
@@ -178,10 +216,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(GroupedGemm p)
       b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * 2u + chunk_log * 16 : kOutOfRange;
     }
 
-    auto issue = [&](int kt, int st) {
+    auto issue = [&](int lk, int st) {
       char* sa = smem + st * C::STAGE_BYTES;
       char* sb = sa + C::A_BYTES;
-      const uint32_t kb = (uint32_t)kt * kRowBytes;
+      const uint32_t kb = (uint32_t)(kt0 + lk) * kRowBytes;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
         load_lds16(rA, sa + (wid * C::A_LOADS + i) * 1024, a_off[i] + kb);
@@ -206,14 +244,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(GroupedGemm p)
     wait_vmcnt<0>();  // stores of the previous tile are out of the way
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < KT) issue(s, s);
+      if (s < KTL) issue(s, s);
 
     const int hi = lane >> 5, l32 = lane & 31;
-    for (int kt = 0; kt < KT; ++kt) {
-      const int ahead = min(KT - 1 - kt, STAGES - 2);  // stages allowed to stay in flight
+    for (int kt = 0; kt < KTL; ++kt) {
+      const int ahead = min(KTL - 1 - kt, STAGES - 2);  // stages allowed to stay in flight
       wait_outstanding<(STAGES - 2) * C::LOADS>(ahead * C::LOADS);
-      __syncthreads();
-      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      wait_lgkmcnt<0>();
+      barrier_keep_loads();  // later stages stay in flight
+      if (kt + STAGES - 1 < KTL) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
       const char* sa = smem + (kt % STAGES) * C::STAGE_BYTES;
       const char* sb = sa + C::A_BYTES;
 #pragma unroll
@@ -253,7 +292,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(GroupedGemm p)
 #pragma unroll
           for (int j = 0; j < C::TN; ++j) {
             const int col = n_t * BN + wn * C::WTN + j * 32 + ec;
-            if (col < p.N) ((float*)p.c)[(out_row0 + lr) * p.ldc + col] = acc[i][j][r];
+            if (col < p.N)
+              ((float*)p.c + ks * p.c_split_stride)[(out_row0 + lr) * p.ldc + col] = acc[i][j][r];
           }
         }
     } else {
@@ -301,37 +341,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(GroupedGemm p)
 }
 
 // ---- prefill kernel ----------------------------------------------------------------------------
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
-// vmcnt[5:4] bits 15:14); "no wait" is the field's maximum
-template <int n>
-__device__ __forceinline__ void wait_lgkmcnt() {
-  static_assert(n >= 0 && n < 16, "lgkmcnt range");
-  __builtin_amdgcn_s_waitcnt(0xf | (0x3 << 14) | (0x7 << 4) | (n << 8));
-}
-
-// Workgroup barrier that leaves outstanding global->LDS loads in flight (the caller has waited
-// for exactly what it needs); also a compiler fence, so no LDS access moves across it.
-__device__ __forceinline__ void barrier_keep_loads() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-// silu(a) = a * sigmoid(a) with the hardware exp2 and reciprocal (the result is rounded to bf16)
-__device__ __forceinline__ float silu_fast(float a) {
-  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
-}
-
-// swizzle of the 16-byte chunks of a 128-byte LDS row: distinct banks for the 8 (and the 16)
-// consecutive rows that one fragment read serves per cycle
-__device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 namespace big {
 constexpr int BM = 256, BN = 256, WM = 2, WN = 4, WAVES = WM * WN, THREADS = WAVES * kWave;
@@ -636,6 +645,7 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   } else {
     max_tiles = (int64_t)((p.static_rows + bm - 1) / bm) * nt;
   }
+  if (p.ksplit > 1) max_tiles *= p.ksplit;
   if (max_tiles > (1 << 30)) max_tiles = 1 << 30;
   const int mt = (int)max_tiles;
   if (kind == GEMM_GATE) {
@@ -656,6 +666,25 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   }
   if (big) return run_big<EPI_BF16, false>(p, mt, num_cus, s);
   return run<32, 256, 1, 4, 4, EPI_BF16, false, 1>(p, mt, num_cus, s);
+}
+
+// ---- split-K reduction: out[i] = sum over s = 0..S-1 of part[s * n + i], in that order ----------
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
+                                                           int64_t n, float* __restrict__ out) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float acc = part[i];
+    for (int s = 1; s < S; ++s) acc += part[s * n + i];
+    out[i] = acc;
+  }
+}
+
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  splitk_reduce_kernel<<<(int)blocks, 256, 0, s>>>(part, S, n, out);
+  return hipGetLastError();
 }
 
 }  // namespace moe
