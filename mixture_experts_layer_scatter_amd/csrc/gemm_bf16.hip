@@ -35,16 +35,14 @@
 // consecutive output columns of one token row and stores them straight from
 // registers; the next tile's first loads go out before that epilogue.  The
 // barrier inside the k-loop leaves the loads of the stage in flight alone
-// (s_barrier without a memory-counter drain).  A wavefront owns the token
-// blocks wm, wm+2, ... of its tile and skips the MFMAs of blocks past the
-// group's last row, so a ragged last row tile costs its rows, not 256.
+// (s_barrier without a memory-counter drain).  Rows past a group's end load as
+// zeros, so every tile costs the same and the workgroups of an XCD stay in
+// step over the panels they share.
 //
 // Small-group kernel (gemm_bf16_kernel, decode and the gate): 32-row tiles,
 // four wavefronts across the columns, four LDS stages to keep weight bytes in
 // flight; the activation tile is staged through LDS for 16-byte row stores.
 #include "common.hpp"
-
-#include <type_traits>
 
 namespace moe {
 
@@ -372,8 +370,7 @@ __global__ __launch_bounds__(big::THREADS) void gemm_big_kernel(GroupedGemm p) {
 
   const int l32 = lane & 31, hi = lane >> 5;
   const int sw = row_swizzle(l32);
-  // wavefront row wm owns token blocks wm, wm + 2, wm + 4, wm + 6 of its tile
-  const uint32_t a_frag = (uint32_t)((wm * 32 + l32) * kRowBytes);
+  const uint32_t a_frag = (uint32_t)((wm * (BM / WM) + l32) * kRowBytes);
   const uint32_t b_frag = (uint32_t)(A_BYTES + (wn * WTN + l32) * kRowBytes);
 
   struct Tile {
@@ -454,30 +451,26 @@ __global__ __launch_bounds__(big::THREADS) void gemm_big_kernel(GroupedGemm p) {
   f32x16 acc[TM][TN];
   bf16x8 fa[2][TM], fb[2][TN];
 
-  // The k-loop with NB active token blocks for this wavefront.  Every NB runs the same loads,
-  // waits and barriers, so the wavefronts of the block stay in step.  At the barrier in the
-  // middle of step kt every wavefront has read all of stage kt, whose slot then takes stage
-  // kt + 2 while the last MFMAs of step kt run from registers.
-  auto kloop = [&](auto nb_c) {
-    constexpr int NB = decltype(nb_c)::value;
-    auto read_frags = [&](const char* st, int kk, int buf) {
-      const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
+  // The k-loop.  At the barrier in the middle of step kt every wavefront has read all of
+  // stage kt, whose slot then takes stage kt + 2 while the last MFMAs of step kt run from
+  // registers.  Every tile costs the same (rows past a group's end are zeros), which keeps the
+  // workgroups of an XCD in step, so the operand panels they share are fetched into L2 once.
+  auto read_frags = [&](const char* st, int kk, int buf) {
+    const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 64 * kRowBytes);
-      if (NB > 0) {
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 32 * kRowBytes);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + coff + j * 32 * kRowBytes);
-      }
-    };
-    // weights as the first operand: D[column][token]
-    auto mfmas = [&](int buf) {
+    for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + coff + j * 32 * kRowBytes);
+  };
+  // weights as the first operand: D[column][token]
+  auto mfmas = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-    };
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  auto kloop = [&]() {
     read_frags(smem, 0, 0);
     if (1 < KT) issue(1, 1, true);
     for (int kt = 0; kt < KT; ++kt) {
@@ -497,9 +490,9 @@ __global__ __launch_bounds__(big::THREADS) void gemm_big_kernel(GroupedGemm p) {
         mfmas(kk & 1);
         // interleave: one MFMA, then one LDS read and (after the barrier) one global load
 #pragma unroll
-        for (int m = 0; m < NB * TN; ++m) {
+        for (int m = 0; m < TM * TN; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (m < NB + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (m < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (kk == KK - 1 && m < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
@@ -521,22 +514,13 @@ __global__ __launch_bounds__(big::THREADS) void gemm_big_kernel(GroupedGemm p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     wait_vmcnt<0>();  // stage 0 (and the previous tile's stores)
     barrier_keep_loads();
-    const int nblocks = (cur.rows_here + 31) >> 5;
-    const int nb = (nblocks - wm + 1) >> 1;  // active token blocks of this wavefront
-    switch (nb) {
-      case 4: kloop(std::integral_constant<int, 4>()); break;
-      case 3: kloop(std::integral_constant<int, 3>()); break;
-      case 2: kloop(std::integral_constant<int, 2>()); break;
-      case 1: kloop(std::integral_constant<int, 1>()); break;
-      default: kloop(std::integral_constant<int, 0>()); break;
-    }
+    kloop();
     // everyone is done with the operand slots and the loads past the last stage have landed
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();
     barrier_keep_loads();
 
     const Tile done = cur;
-    const int done_nb = nb;
     it += nx;
     const bool more = locate(it, cur);
     if (more) {  // the next tile's first stage loads while this tile's results go out
@@ -544,13 +528,12 @@ __global__ __launch_bounds__(big::THREADS) void gemm_big_kernel(GroupedGemm p) {
       issue(0, 0, true);
     }
 
-    // epilogue: lane holds token l32 of block (2i + wm) and columns 8q + 4hi + (0..3) of
-    // each 32-column block j
+    // epilogue: lane holds token l32 of block i and columns 8q + 4hi + (0..3) of each
+    // 32-column block j
     const int64_t out_row0 = (int64_t)done.row_base + done.m0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      if (i >= done_nb) break;
-      const int tok = (2 * i + wm) * 32 + l32;
+      const int tok = wm * (BM / WM) + i * 32 + l32;
       if (tok >= done.rows_here) continue;
       uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
       if constexpr (EPI == EPI_SWIGLU) {
