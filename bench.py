@@ -134,7 +134,11 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["traffic"] = profiled_traffic(w.name)
-    roof["kernel"] = "gemm_bf16_kernel (grouped gate-up + SiLU*mul)"
+    # the library takes 256-row tiles when a group holds >= 128 rows on average
+    if (w.T * w.k) // w.E >= 128:
+        roof["kernel"] = "gemm_big_kernel (grouped gate-up + SiLU*mul, 256x256 tiles)"
+    else:
+        roof["kernel"] = "gemm_bf16_kernel<32,256,...> (grouped gate-up + SiLU*mul, 32-row tiles)"
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
     layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
