@@ -17,7 +17,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Byte layout of the workspace; one layout serves every call.
 struct Layout {
-  size_t gate_part, logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn, pos,
+  size_t tail, gate_part, logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn, pos,
       dropped, row_token, act, yp, yps, total;
 };
 
@@ -48,6 +48,15 @@ Layout layout(const moe_dims_t* d) {
     o += align_up(bytes ? bytes : 1);
     return at;
   };
+  // partial tiles of the grouped GEMMs' split last round (sized for the larger tile shape the
+  // routed experts or a separate shared expert can take)
+  if (d->dtype == MOE_BF16) {
+    const int64_t avg = (int64_t)d->T * d->k / d->E;
+    const int big_rows = (avg >= 128 || (d->I_shared > 0 && d->T >= 128)) ? 128 : 0;
+    L.tail = take(gemm_tail_bytes(big_rows));
+  } else {
+    L.tail = take(0);
+  }
   const int gs = gate_splits(d);
   L.gate_part = take(gs > 1 ? (size_t)gs * T * E * 4 : 0);
   L.logits = take(T * E * 4);
@@ -174,7 +183,8 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
                    int64_t a_rows, int64_t max_rows, const int32_t* offsets, int G, int G_routed,
                    const void* w1, const void* w3, const void* w2, const void* e1,
                    const void* e3, const void* e2, void* act, void* out, int32_t* ts_gu,
-                   int32_t* ts_dn, int avg_rows, hipStream_t s, void* const* ev = nullptr) {
+                   int32_t* ts_dn, int avg_rows, float* tail, hipStream_t s,
+                   void* const* ev = nullptr) {
   const bool bf16 = d->dtype == MOE_BF16;
   int bm_gu, nt_gu, bm_dn, nt_dn;
   if (bf16) {
@@ -206,6 +216,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   gu.G = G;
   gu.G_routed = G_routed;
   gu.tile_start = ts_gu;
+  gu.tail_part = bf16 ? tail : nullptr;
 
   GroupedGemm dn = {};
   dn.a = act;
@@ -222,6 +233,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   dn.G = G;
   dn.G_routed = G_routed;
   dn.tile_start = ts_dn;
+  dn.tail_part = bf16 ? tail : nullptr;
 
   const int cus = num_cus();
   const int64_t mt_gu = (ceil_div64(max_rows, bm_gu) + G) * nt_gu;
@@ -339,7 +351,7 @@ moe_status_t moe_expert_ffn(const moe_dims_t* d, const void* x_packed, const int
   const int avg = (int)(n / d->E);
   MOE_TRY(run_ffn(d, d->I, x_packed, nullptr, n, n, offsets, d->E, d->E, w1, w3, w2, nullptr,
                   nullptr, nullptr, at<void>(ws, L.act), y_packed, at<int32_t>(ws, L.ts_gu),
-                  at<int32_t>(ws, L.ts_dn), avg, (hipStream_t)stream));
+                  at<int32_t>(ws, L.ts_dn), avg, at<float>(ws, L.tail), (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -404,7 +416,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
   MOE_TRY(run_ffn(d, d->I, x, row_token, T, max_rows, offsets, G, E, w1, w3, w2,
                   fold ? ws1 : nullptr, fold ? ws3 : nullptr, fold ? ws2 : nullptr,
                   at<void>(ws, L.act), yp, at<int32_t>(ws, L.ts_gu), at<int32_t>(ws, L.ts_dn), avg,
-                  s, ev));
+                  at<float>(ws, L.tail), s, ev));
   const void* ys = nullptr;
   const int32_t* ys_row0 = nullptr;
   if (fold) {
@@ -419,7 +431,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
     MOE_TRY(hipGetLastError());
     MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 0, ws1, ws3, ws2, nullptr, nullptr,
                     nullptr, at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
-                    at<int32_t>(ws, L.ts_dn), T, s));
+                    at<int32_t>(ws, L.ts_dn), T, at<float>(ws, L.tail), s));
     ys = at<void>(ws, L.yps);
   }
   // 6. weighted combine back into token order

@@ -98,7 +98,12 @@ struct GroupedGemm {
   const int32_t* tile_start; // [G+1] device tile map, or null with offsets == null
   int ksplit;                // > 1: split the reduction (fp32 output only), partial s at
   int64_t c_split_stride;    //      c + s * c_split_stride (elements)
+  // Split of the last, partly filled round of tiles (each XCD's chunk): when set, a tile of
+  // that round is reduced by up to 4 workgroups into fp32 partials here, which a second
+  // kernel adds in a fixed order before the epilogue.  Room: 8 * kTailPieces tiles.
+  float* tail_part;
 };
+constexpr int kTailPieces = 32;  // partial tiles per XCD the tail buffer holds
 
 // bf16 MFMA paths
 enum GemmKind { GEMM_GATE = 0, GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
@@ -106,6 +111,8 @@ enum GemmKind { GEMM_GATE = 0, GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
 void gemm_bf16_tiling(GemmKind kind, int max_rows_per_group, int N, int* bm, int* nt);
 hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& g, int max_rows_per_group,
                             int num_cus, hipStream_t s);
+// bytes of GroupedGemm::tail_part needed by launch_gemm_bf16 for this kind and group size
+size_t gemm_tail_bytes(int avg_rows_per_group);
 
 // out[i] = sum_s part[s * n + i] (fixed order)
 hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out, hipStream_t s);

@@ -125,6 +125,135 @@ struct TileShape {
 using PrefillShape = TileShape<256, 256, 2, 4, 2>;
 using DecodeShape = TileShape<32, 256, 1, 4, 4>;
 
+// ---- tile bookkeeping shared by the GEMM and its tail reduction ---------------------------------
+
+struct TileLoc {
+  int row_base, m0, rows_here, n_t, g;
+};
+
+// tile `tile` of the (unsplit) tile list: its group, row block and column block
+template <class SH, int GN>
+__device__ __forceinline__ TileLoc locate_tile(const GroupedGemm& p, int tile) {
+  int g = 0, row_base = 0, rows = p.static_rows, li = tile;
+  if (p.tile_start) {
+    int lo = 0, hi2 = p.G;  // largest g with tile_start[g] <= tile
+    while (hi2 - lo > 1) {
+      const int mid = (lo + hi2) >> 1;
+      if (p.tile_start[mid] <= tile) lo = mid;
+      else hi2 = mid;
+    }
+    g = lo;
+    li = tile - p.tile_start[g];
+    row_base = p.offsets[g];
+    rows = p.offsets[g + 1] - row_base;
+  }
+  const int mt = (rows + SH::BM - 1) / SH::BM;
+  const int nblk = li / (mt * GN), rem = li % (mt * GN);
+  TileLoc t;
+  t.g = g;
+  t.row_base = row_base;
+  t.m0 = (rem % mt) * SH::BM;
+  t.n_t = nblk * GN + rem / mt;
+  t.rows_here = min(SH::BM, rows - t.m0);
+  return t;
+}
+
+// XCD x takes tiles [lo, lo + n) of the list, nx workgroups at a time.  When the last round is
+// at most half full and a tail buffer is given, each of its `tail` tiles is cut into `pieces`
+// k-ranges so the round's workgroups stay busy; the GEMM then has full * nx + tail * pieces
+// work items in this XCD.
+struct TailPlan {
+  int lo, n, full, tail, pieces;
+};
+__device__ __forceinline__ TailPlan tail_plan(int total, int xcd, int nx, int kt, bool enabled) {
+  const int per_xcd = (total + 7) / 8;
+  TailPlan t;
+  t.lo = xcd * per_xcd;
+  t.n = max(0, min(per_xcd, total - t.lo));
+  t.full = t.n / nx;
+  t.tail = t.n - t.full * nx;
+  t.pieces = 1;
+  if (enabled && t.tail > 0 && 2 * t.tail <= nx) {
+    int ks = min(4, nx / t.tail);
+    while (ks > 1 && (kt / ks < 8 || t.tail * ks > kTailPieces)) --ks;
+    t.pieces = ks;
+  }
+  return t;
+}
+
+// The epilogue: lane holds token l32 of block i and columns 8q + 4hi + (0..3) of each
+// 32-column block j (the weights were the MFMA's first operand: D[column][token]).
+template <class SH, int EPI>
+__device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& t, int ks,
+                                           const f32x16 (&acc)[SH::TM][SH::TN], int wm, int wn,
+                                           int l32, int hi, int i_only = -1) {
+  constexpr int BN = SH::BN, TM = SH::TM, TN = SH::TN;
+  const int64_t out_row0 = (int64_t)t.row_base + t.m0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i_only >= 0 && i != i_only) continue;
+    const int tok = wm * SH::WTM + i * 32 + l32;
+    if (tok >= t.rows_here) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
+      // blocks j (W1) and j + 1 (W3) hold the same 32 columns
+#pragma unroll
+      for (int j = 0; j < TN; j += 2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = t.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32 + 8 * q + 4 * hi;
+          if (col < p.N) {
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = silu_fast(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
+            uint2 v;
+            v.x = pack_bf16x2(h[0], h[1]);
+            v.y = pack_bf16x2(h[2], h[3]);
+            *(uint2*)(crow + col) = v;
+          }
+        }
+    } else if constexpr (EPI == EPI_BF16) {
+      uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
+          if (col < p.N) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+            v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *(uint2*)(crow + col) = v;
+          }
+        }
+    } else {
+      float* crow = (float*)p.c + ks * p.c_split_stride + (out_row0 + tok) * p.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
+          if (col + 3 < p.N && (p.ldc & 3) == 0) {
+            *(float4*)(crow + col) = make_float4(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
+                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < p.N) crow[col + e] = acc[i][j][4 * q + e];
+          }
+        }
+    }
+  }
+}
+
+// fp32 partial tile `slot` of XCD `xcd` in the tail buffer, laid out [block i][block j][quad]
+// [thread][4]: a thread moves 16 bytes at a time and a wavefront 1 KB contiguous runs
+template <class SH>
+__device__ __forceinline__ float4* tail_slot(const GroupedGemm& p, int xcd, int slot) {
+  constexpr int64_t kRegs = SH::TM * SH::TN * 16;
+  return (float4*)(p.tail_part + ((int64_t)xcd * kTailPieces + slot) * kRegs * SH::THREADS);
+}
+
 template <class SH, int EPI, bool GATHER, int GN>
 __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, L = SH::L;
@@ -140,9 +269,9 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   // split-K: ksplit consecutive copies of the tile list; copy ks reduces over its share of the
   // k-steps into the partial output c + ks * c_split_stride
   const int ks_n = p.ksplit > 1 ? p.ksplit : 1;
-  const int total = total_base * ks_n;
   const int nx = gridDim.x / 8, xcd = blockIdx.x % 8;
-  const int per_xcd = (total + 7) / 8;
+  const TailPlan plan = tail_plan(total_base * ks_n, xcd, nx, KT, p.tail_part && ks_n == 1);
+  const int items = plan.pieces > 1 ? plan.full * nx + plan.tail * plan.pieces : plan.n;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * 2));
 
   const int l32 = lane & 31, hi = lane >> 5;
@@ -151,36 +280,29 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   const uint32_t b_frag = (uint32_t)(SH::A_BYTES + (wn * SH::WTN + l32) * kRowBytes);
 
   struct Tile {
-    int row_base, m0, rows_here, n_t, g, kt0, ktn, ks;
+    TileLoc loc;
+    int kt0, ktn, ks, slot;  // slot >= 0: a piece of a split tail tile, partial goes there
   };
   auto locate = [&](int it, Tile& t) -> bool {
-    if (it >= per_xcd) return false;
-    const int tile_all = xcd * per_xcd + it;
-    if (tile_all >= total) return false;
-    const int ks = tile_all / total_base, tile = tile_all - ks * total_base;
-    int g = 0, row_base = 0, rows = p.static_rows, li = tile;
-    if (p.tile_start) {
-      int lo = 0, hi2 = p.G;  // largest g with tile_start[g] <= tile
-      while (hi2 - lo > 1) {
-        const int mid = (lo + hi2) >> 1;
-        if (p.tile_start[mid] <= tile) lo = mid;
-        else hi2 = mid;
-      }
-      g = lo;
-      li = tile - p.tile_start[g];
-      row_base = p.offsets[g];
-      rows = p.offsets[g + 1] - row_base;
+    if (it >= items) return false;
+    int tile_all = plan.lo + it, kt0 = 0, ktn = KT, slot = -1;
+    if (plan.pieces > 1 && it >= plan.full * nx) {
+      const int j = it - plan.full * nx, piece = j % plan.pieces;
+      tile_all = plan.lo + plan.full * nx + j / plan.pieces;
+      kt0 = (int)((int64_t)piece * KT / plan.pieces);
+      ktn = (int)((int64_t)(piece + 1) * KT / plan.pieces) - kt0;
+      slot = j;
     }
-    const int mt = (rows + BM - 1) / BM;
-    const int nblk = li / (mt * GN), rem = li % (mt * GN);
-    t.g = g;
-    t.row_base = row_base;
-    t.m0 = (rem % mt) * BM;
-    t.n_t = nblk * GN + rem / mt;
-    t.rows_here = min(BM, rows - t.m0);
+    const int ks = tile_all / total_base, tile = tile_all - ks * total_base;
+    if (ks_n > 1) {
+      kt0 = (int)((int64_t)ks * KT / ks_n);
+      ktn = (int)((int64_t)(ks + 1) * KT / ks_n) - kt0;
+    }
+    t.loc = locate_tile<SH, GN>(p, tile);
     t.ks = ks;
-    t.kt0 = (int)((int64_t)ks * KT / ks_n);
-    t.ktn = (int)((int64_t)(ks + 1) * KT / ks_n) - t.kt0;
+    t.kt0 = kt0;
+    t.ktn = ktn;
+    t.slot = slot;
     return true;
   };
 
@@ -191,12 +313,12 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   auto setup = [&](const Tile& t) {
     kt0 = t.kt0;
     ktn = t.ktn;
-    const bool extra = p.tile_start && t.g >= p.G_routed;
+    const bool extra = p.tile_start && t.loc.g >= p.G_routed;
     const char* bbase =
-        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.g * p.b_stride * 2);
+        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * 2);
     const char* b2base = bbase;
     if (EPI == EPI_SWIGLU)
-      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)t.g * p.b_stride * 2);
+      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * 2);
     const uint32_t b_bytes = (uint32_t)((int64_t)p.N * K * 2);
     rB = make_rsrc(bbase, b_bytes);
     rB2 = make_rsrc(b2base, b_bytes);
@@ -205,8 +327,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       const int r = (wid * SH::A_LOADS + i) * RPL + lane / 8;
       const int c = (lane & 7) ^ row_swizzle(r);
       uint32_t off = kOutOfRange;
-      if (r < t.rows_here) {
-        const int prow = t.row_base + t.m0 + r;
+      if (r < t.loc.rows_here) {
+        const int prow = t.loc.row_base + t.loc.m0 + r;
         const int64_t src = GATHER ? (int64_t)p.row_map[prow] : (int64_t)prow;
         off = (uint32_t)(src * K * 2) + c * 16;
       }
@@ -216,7 +338,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     for (int i = 0; i < SH::B_LOADS; ++i) {
       const int n = (wid * SH::B_LOADS + i) * RPL + lane / 8;
       const int c = (lane & 7) ^ row_swizzle(n);
-      const int src = EPI == EPI_SWIGLU ? t.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.n_t * BN + n;
+      const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
       b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * 2u + c * 16 : kOutOfRange;
     }
   };
@@ -318,65 +440,62 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       prologue();
     }
 
-    // epilogue: lane holds token l32 of block i and columns 8q + 4hi + (0..3) of each
-    // 32-column block j
-    const int64_t out_row0 = (int64_t)done.row_base + done.m0;
+    if (done.slot >= 0) {
+      // a piece of a split tail tile: park the fp32 partial for the tail reduction
+      float4* dst = tail_slot<SH>(p, xcd, done.slot) + tid;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int tok = wm * SH::WTM + i * 32 + l32;
-      if (tok >= done.rows_here) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
-        uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
-        // blocks j (W1) and j + 1 (W3) hold the same 32 columns
-#pragma unroll
-        for (int j = 0; j < TN; j += 2)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = done.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32 + 8 * q + 4 * hi;
-            if (col < p.N) {
-              float h[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) h[e] = silu_fast(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
-              uint2 v;
-              v.x = pack_bf16x2(h[0], h[1]);
-              v.y = pack_bf16x2(h[2], h[3]);
-              *(uint2*)(crow + col) = v;
-            }
-          }
-      } else if constexpr (EPI == EPI_BF16) {
-        uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = done.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
-            if (col < p.N) {
-              uint2 v;
-              v.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-              v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              *(uint2*)(crow + col) = v;
-            }
-          }
-      } else {
-        float* crow = (float*)p.c + done.ks * p.c_split_stride + (out_row0 + tok) * p.ldc;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = done.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
-            if (col + 3 < p.N && (p.ldc & 3) == 0) {
-              *(float4*)(crow + col) = make_float4(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
-                                                   acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (col + e < p.N) crow[col + e] = acc[i][j][4 * q + e];
-            }
-          }
-      }
+          for (int q = 0; q < 4; ++q)
+            dst[((i * TN + j) * 4 + q) * SH::THREADS] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    } else {
+      store_tile<SH, EPI>(p, done.loc, done.ks, acc, wm, wn, l32, hi);
     }
     if (!more) break;
   }
+}
+
+// The split tail tiles: add each tile's fp32 partials in piece order, then the epilogue.  One
+// workgroup per (XCD, tail tile, token block i), so the reduction spreads over many CUs.
+template <class SH, int EPI, int GN>
+__global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, int nx) {
+  constexpr int TM = SH::TM, TN = SH::TN;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wid / SH::WN, wn = wid % SH::WN;
+  const int xcd = blockIdx.x % 8, t = (blockIdx.x / 8) % kTailPieces, ib = blockIdx.x / (8 * kTailPieces);
+  const TailPlan plan = tail_plan(p.tile_start[p.G], xcd, nx, p.K / kBK, true);
+  if (plan.pieces <= 1 || t >= plan.tail) return;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i != ib) continue;
+    for (int piece = 0; piece < plan.pieces; ++piece) {
+      const float4* src = tail_slot<SH>(p, xcd, t * plan.pieces + piece) + tid;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = src[((i * TN + j) * 4 + q) * SH::THREADS];
+          if (piece == 0) {
+            acc[i][j][4 * q] = v.x;
+            acc[i][j][4 * q + 1] = v.y;
+            acc[i][j][4 * q + 2] = v.z;
+            acc[i][j][4 * q + 3] = v.w;
+          } else {
+            acc[i][j][4 * q] += v.x;
+            acc[i][j][4 * q + 1] += v.y;
+            acc[i][j][4 * q + 2] += v.z;
+            acc[i][j][4 * q + 3] += v.w;
+          }
+        }
+    }
+  }
+  const TileLoc loc = locate_tile<SH, GN>(p, plan.lo + plan.full * nx + t);
+  store_tile<SH, EPI>(p, loc, 0, acc, wm, wn, lane & 31, lane >> 5, ib);
 }
 
 template <class SH, int EPI, bool GATHER, int GN>
@@ -393,7 +512,12 @@ static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStrea
   int grid = num_cus * per_cu;
   if (grid > max_tiles) grid = max_tiles;
   grid = (grid + 7) / 8 * 8;
-  kern<<<grid, SH::THREADS, SH::LDS, s>>>(p);
+  GroupedGemm q = p;
+  if (!q.tile_start || q.ksplit > 1 || EPI == EPI_F32 || grid / 8 > kTailPieces) q.tail_part = nullptr;
+  kern<<<grid, SH::THREADS, SH::LDS, s>>>(q);
+  e = hipGetLastError();
+  if (e != hipSuccess || !q.tail_part) return e;
+  gemm_tail_kernel<SH, EPI, GN><<<8 * kTailPieces * SH::TM, SH::THREADS, 0, s>>>(q, grid / 8);
   return hipGetLastError();
 }
 
@@ -409,6 +533,13 @@ void gemm_bf16_tiling(GemmKind kind, int avg_rows_per_group, int N, int* bm, int
   *bm = big ? PrefillShape::BM : DecodeShape::BM;
   const int bn = big ? PrefillShape::BN : DecodeShape::BN;
   *nt = kind == GEMM_GATE_UP ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
+}
+
+size_t gemm_tail_bytes(int avg_rows_per_group) {
+  const bool big = avg_rows_per_group >= 128;
+  const size_t tile = big ? (size_t)PrefillShape::BM * PrefillShape::BN
+                          : (size_t)DecodeShape::BM * DecodeShape::BN;
+  return 8 * (size_t)kTailPieces * tile * sizeof(float);
 }
 
 hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_per_group,

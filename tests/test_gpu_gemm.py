@@ -97,6 +97,21 @@ def test_expert_ffn_bf16(counts, H, I):
     assert (row_err <= 2e-2).all()
 
 
+@pytest.mark.parametrize("counts,H,I", [
+    ([300, 280, 270, 310], 2048, 1024),   # the last, partly filled round of tiles is split
+    ([700, 1, 650, 515], 1024, 2048),     # over k-ranges and added back by a second kernel
+])
+def test_expert_ffn_bf16_split_tail(counts, H, I):
+    need_gpu()
+    log(f"expert_ffn bf16 (split tail round) counts={counts} H={H} I={I}")
+    got, ref = _ffn_case(counts, H, I, "bf16", seed=7)
+    err = rel_l2(got, ref)
+    row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    log(f"  rel-L2 {err:.3g}, worst row {row_err.max():.3g}")
+    assert err <= 2e-2
+    assert (row_err <= 2e-2).all()
+
+
 @pytest.mark.parametrize("counts,H,I", [([64, 0, 33, 100], 128, 256), ([3, 5], 100, 30)])
 def test_expert_ffn_f32(counts, H, I):
     need_gpu()
