@@ -186,6 +186,9 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
                    int32_t* ts_dn, int avg_rows, float* tail, hipStream_t s,
                    void* const* ev = nullptr) {
   const bool bf16 = d->dtype == MOE_BF16;
+  // groups past G_routed take the extra weights; there must be some for them
+  if (G_routed < 0 || G_routed > G || (G > G_routed && (!e1 || !e3 || !e2)) || !w1 || !w3 || !w2)
+    return hipErrorInvalidValue;
   int bm_gu, nt_gu, bm_dn, nt_dn;
   if (bf16) {
     gemm_bf16_tiling(GEMM_GATE_UP, avg_rows, I, &bm_gu, &nt_gu);
@@ -429,7 +432,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
     int32_t* off2 = at<int32_t>(ws, L.raw);  // two ints: [0, T]
     whole_range_kernel<<<1, 1, 0, s>>>(off2, T);
     MOE_TRY(hipGetLastError());
-    MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 0, ws1, ws3, ws2, nullptr, nullptr,
+    MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 1, ws1, ws3, ws2, nullptr, nullptr,
                     nullptr, at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
                     at<int32_t>(ws, L.ts_dn), T, at<float>(ws, L.tail), s));
     ys = at<void>(ws, L.yps);

@@ -125,3 +125,33 @@ def test_deterministic():
     b = run_gpu(w, t)
     for k in ("y", "logits", "topk_ids", "topk_w", "pos"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def _random_workloads(n=14, seed=2024):
+    """Seeded mix of small layer shapes: both storage types, E from 1 to 130, every k, a shared
+    expert of the routed size or of another size, capacity factors that drop slots, the Zipf
+    bias, raw softmax weights, and token counts from 1 up."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "f32" if i % 4 == 0 else "bf16"
+        H = int(rng.choice([64, 128, 256, 512]))
+        E = int(rng.choice([1, 3, 16, 64, 130]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        I = int(rng.choice([64, 128, 192]))
+        shared = int(rng.choice([0, I, 64 if I != 64 else 128]))
+        cf = [None, 0.5, 1.0, 1.25][int(rng.integers(0, 4))]
+        zipf = 1.2 if rng.random() < 0.3 else None
+        T = int(rng.choice([1, 7, 100, 333, 1000]))
+        out.append(moe_synth.Workload(f"random{i}", 100 + i, T=T, H=H, E=E, k=k, I=I,
+                                      I_shared=shared, dtype=dtype, capacity_factor=cf,
+                                      zipf_s=zipf, renormalize=int(rng.random() < 0.8)))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_workloads(), ids=lambda w: (
+    f"{w.name}-{w.dtype}-T{w.T}-H{w.H}-E{w.E}-k{w.k}-I{w.I}-Is{w.I_shared}-cf{w.capacity_factor}"
+    f"-z{w.zipf_s}-r{w.renormalize}"))
+def test_random_shapes_every_token(w):
+    need_gpu()
+    check_layer(w)
