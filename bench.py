@@ -135,10 +135,13 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["traffic"] = profiled_traffic(w.name)
     # the library takes 256-row tiles when a group holds >= 128 rows on average
+    # (the timed span is the grouped GEMM plus the reduction of its split last round of tiles)
     if (w.T * w.k) // w.E >= 128:
-        roof["kernel"] = "gemm_big_kernel (grouped gate-up + SiLU*mul, 256x256 tiles)"
+        roof["kernel"] = ("gemm_kernel<TileShape<256,256,2,4,2>, SwiGLU> + gemm_tail_kernel "
+                          "(grouped gate-up, 256x256 tiles)")
     else:
-        roof["kernel"] = "gemm_bf16_kernel<32,256,...> (grouped gate-up + SiLU*mul, 32-row tiles)"
+        roof["kernel"] = ("gemm_kernel<TileShape<32,256,1,4,4>, SwiGLU> + gemm_tail_kernel "
+                          "(grouped gate-up, 32-row tiles)")
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
     layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
@@ -176,7 +179,7 @@ def kernel_source_digest():
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "common.hpp"):
+    for f in ("gemm_bf16.hip", "common.hpp", "api.hip"):
         with open(os.path.join(ROOT, "mixture_experts_layer_scatter_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
