@@ -311,8 +311,10 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   __amdgpu_buffer_rsrc_t rB, rB2;
   int kt0 = 0, ktn = 0;
   auto setup = [&](const Tile& t) {
-    kt0 = t.kt0;
-    ktn = t.ktn;
+    // uniform, but the 64-bit divisions that split k leave them in VGPRs; a VGPR soffset would
+    // make every buffer load a readfirstlane loop
+    kt0 = __builtin_amdgcn_readfirstlane(t.kt0);
+    ktn = __builtin_amdgcn_readfirstlane(t.ktn);
     const bool extra = p.tile_start && t.loc.g >= p.G_routed;
     const char* bbase =
         (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * 2);
