@@ -38,7 +38,9 @@ def lib():
         L.oracle_gate.restype = None
         L.oracle_gate.argtypes = [_i64, _i64, _i64, C.c_int, _p, _p, _p]
         L.oracle_route.restype = None
-        L.oracle_route.argtypes = [_i64, _i64, _i64, _p, _p, C.c_int, _p, _p, _p]
+        L.oracle_route.argtypes = [_i64, _i64, _i64, _p, _p, C.c_int, C.c_int, _p, _p, _p]
+        L.oracle_load_stats.restype = None
+        L.oracle_load_stats.argtypes = [_i64, _i64, _i64, _i32, _p, _p, _p, _p, _p]
         L.oracle_permute.restype = _i64
         L.oracle_permute.argtypes = [_i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _p]
         L.oracle_expert_ffn.restype = None
@@ -46,7 +48,7 @@ def lib():
         L.oracle_combine.restype = None
         L.oracle_combine.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p]
         L.oracle_layer.restype = _i64
-        L.oracle_layer.argtypes = [_i64] * 6 + [_i32, C.c_int, C.c_int] + [_p] * 15
+        L.oracle_layer.argtypes = [_i64] * 6 + [_i32, C.c_int, C.c_int, C.c_int] + [_p] * 15
         _lib = L
     return _lib
 
@@ -90,7 +92,11 @@ def gate(x: np.ndarray, wg: np.ndarray) -> np.ndarray:
     return out
 
 
-def route(logits: np.ndarray, k: int, bias: np.ndarray | None = None, renormalize: int = 1):
+BIAS_SOFTMAX, BIAS_SELECT = 0, 1
+
+
+def route(logits: np.ndarray, k: int, bias: np.ndarray | None = None, renormalize: int = 1,
+          bias_mode: int = BIAS_SOFTMAX):
     """Returns (ids int32 [T,k], w float64 [T,k], margin float64 [T])."""
     logits = _c(logits, np.float32)
     bias = _c(bias, np.float32)
@@ -98,9 +104,29 @@ def route(logits: np.ndarray, k: int, bias: np.ndarray | None = None, renormaliz
     ids = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
     margin = np.empty((T,), np.float64)
-    lib().oracle_route(T, E, k, _ptr(logits), _ptr(bias), int(renormalize), _ptr(ids), _ptr(w),
-                       _ptr(margin))
+    lib().oracle_route(T, E, k, _ptr(logits), _ptr(bias), int(renormalize), int(bias_mode),
+                       _ptr(ids), _ptr(w), _ptr(margin))
     return ids, w, margin
+
+
+def load_stats(ids: np.ndarray, E: int, capacity: int = -1, bias_next: bool = False):
+    """Per-expert picks and the load statistics of a routing decision (oracle_load_stats);
+    with bias_next, also the next balancing bias (float32 [E], needs capacity >= 1)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    raw = np.empty(E, np.int32)
+    ints = np.empty(6, np.int64)
+    reals = np.empty(5, np.float64)
+    b = np.empty(E, np.float32) if bias_next else None
+    lib().oracle_load_stats(T, E, k, int(capacity), _ptr(ids), _ptr(raw), _ptr(ints), _ptr(reals),
+                            _ptr(b))
+    out = dict(raw=raw, picks=int(ints[0]), dropped=int(ints[1]), max_count=int(ints[2]),
+               hottest=int(ints[3]), min_count=int(ints[4]), idle=int(ints[5]),
+               mean=float(reals[0]), stddev=float(reals[1]), cv=float(reals[2]),
+               max_over_mean=float(reals[3]), drop_rate=float(reals[4]))
+    if bias_next:
+        out["bias_next"] = b
+    return out
 
 
 def permute(ids: np.ndarray, E: int, capacity: int = -1, active: np.ndarray | None = None):
@@ -150,7 +176,8 @@ def combine(yp: np.ndarray, pos: np.ndarray, w: np.ndarray, ys: np.ndarray | Non
     return y
 
 
-def layer(x, wg, w1, w3, w2, k, capacity=-1, renormalize=1, bias=None, shared=None):
+def layer(x, wg, w1, w3, w2, k, capacity=-1, renormalize=1, bias=None, shared=None,
+          bias_mode=BIAS_SOFTMAX):
     """Whole layer; returns (y float64 [T,H], info dict)."""
     x, wg, w1, w3, w2 = _c(x), _c(wg), _c(w1), _c(w3), _c(w2)
     bias = _c(bias, np.float32)
@@ -169,7 +196,8 @@ def layer(x, wg, w1, w3, w2, k, capacity=-1, renormalize=1, bias=None, shared=No
     w = np.empty((T, k), np.float64)
     pos = np.empty((T, k), np.int32)
     counts = np.empty(E, np.int32)
-    nd = lib().oracle_layer(T, H, E, k, I, Is, int(capacity), int(renormalize), dt, _ptr(x),
+    nd = lib().oracle_layer(T, H, E, k, I, Is, int(capacity), int(renormalize), int(bias_mode),
+                            dt, _ptr(x),
                             _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
                             _ptr(ws3), _ptr(ws2), _ptr(y), _ptr(logits), _ptr(ids), _ptr(w),
                             _ptr(pos), _ptr(counts))

@@ -53,8 +53,9 @@ static int before(float ka, int64_t a, float kb, int64_t b) {
 }
 
 void oracle_route(int64_t T, int64_t E, int64_t k, const float* logits, const float* bias,
-                  int renormalize, int32_t* ids, double* w, double* margin) {
+                  int renormalize, int bias_mode, int32_t* ids, double* w, double* margin) {
     float* key = (float*)malloc((size_t)E * sizeof(float));
+    double* val = (double*)malloc((size_t)E * sizeof(double));
     unsigned char* taken = (unsigned char*)malloc((size_t)E);
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t e = 0; e < E; ++e) {
@@ -85,19 +86,67 @@ void oracle_route(int64_t T, int64_t E, int64_t k, const float* logits, const fl
                 margin[t] = (double)key[ids[t * k + k - 1]] - (double)key[next];
             }
         }
-        /* softmax over all experts: p_e = exp(l'_e - m) / sum_e' exp(l'_e' - m) */
-        double m = (double)key[ids[t * k]];
+        /* the values the softmax is taken of: the keys, or with a selection-only bias the
+           logits themselves */
+        const int sel_only = bias && bias_mode == ORACLE_BIAS_SELECT;
+        for (int64_t e = 0; e < E; ++e) val[e] = sel_only ? (double)logits[t * E + e] : (double)key[e];
+        /* softmax over all experts: p_e = exp(v_e - m) / sum_e' exp(v_e' - m), m the row max */
+        double m = val[0];
+        for (int64_t e = 1; e < E; ++e)
+            if (val[e] > m) m = val[e];
         double full = 0.0;
-        for (int64_t e = 0; e < E; ++e) full += exp((double)key[e] - m);
+        for (int64_t e = 0; e < E; ++e) full += exp(val[e] - m);
         double picked = 0.0;
-        for (int64_t j = 0; j < k; ++j) picked += exp((double)key[ids[t * k + j]] - m) / full;
+        for (int64_t j = 0; j < k; ++j) picked += exp(val[ids[t * k + j]] - m) / full;
         for (int64_t j = 0; j < k; ++j) {
-            double p = exp((double)key[ids[t * k + j]] - m) / full;
+            double p = exp(val[ids[t * k + j]] - m) / full;
             w[t * k + j] = renormalize ? p / picked : p;
         }
     }
     free(key);
+    free(val);
     free(taken);
+}
+
+void oracle_load_stats(int64_t T, int64_t E, int64_t k, int32_t capacity, const int32_t* ids,
+                       int32_t* raw, int64_t* ints, double* reals, float* bias_next) {
+    for (int64_t e = 0; e < E; ++e) raw[e] = 0;
+    for (int64_t s = 0; s < T * k; ++s)
+        if (ids[s] >= 0 && ids[s] < E) raw[ids[s]]++;
+    int64_t picks = 0, dropped = 0, idle = 0, hottest = 0, max_count = raw[0], min_count = raw[0];
+    for (int64_t e = 0; e < E; ++e) {
+        picks += raw[e];
+        if (capacity >= 0 && raw[e] > capacity) dropped += raw[e] - capacity;
+        if (raw[e] == 0) idle++;
+        if (raw[e] > max_count) {
+            max_count = raw[e];
+            hottest = e;
+        }
+        if (raw[e] < min_count) min_count = raw[e];
+    }
+    double mean = (double)picks / (double)E;
+    double ss = 0.0;
+    for (int64_t e = 0; e < E; ++e) ss += ((double)raw[e] - mean) * ((double)raw[e] - mean);
+    double stddev = sqrt(ss / (double)E);
+    ints[0] = picks;
+    ints[1] = dropped;
+    ints[2] = max_count;
+    ints[3] = hottest;
+    ints[4] = min_count;
+    ints[5] = idle;
+    reals[0] = mean;
+    reals[1] = stddev;
+    reals[2] = mean > 0.0 ? stddev / mean : 0.0;
+    reals[3] = mean > 0.0 ? (double)max_count / mean : 0.0;
+    reals[4] = picks > 0 ? (double)dropped / (double)picks : 0.0;
+    if (bias_next && capacity >= 1) {
+        for (int64_t e = 0; e < E; ++e) {
+            double b = ((double)capacity - (double)raw[e]) / (double)capacity;
+            if (b < -1.0) b = -1.0;
+            if (b > 1.0) b = 1.0;
+            bias_next[e] = (float)b;
+        }
+    }
 }
 
 int64_t oracle_permute(int64_t T, int64_t E, int64_t k, int32_t capacity, const int32_t* ids,
@@ -187,7 +236,8 @@ void oracle_combine(int64_t T, int64_t H, int64_t k, const double* yp, const int
 }
 
 int64_t oracle_layer(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is,
-                     int32_t capacity, int renormalize, int dt, const void* x, const void* wg,
+                     int32_t capacity, int renormalize, int bias_mode, int dt, const void* x,
+                     const void* wg,
                      const float* bias, const void* w1, const void* w3, const void* w2,
                      const void* ws1, const void* ws3, const void* ws2, double* y,
                      float* logits_out, int32_t* ids_out, double* w_out, int32_t* pos_out,
@@ -207,7 +257,7 @@ int64_t oracle_layer(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int6
     double* ys = NULL;
 
     oracle_gate(T, H, E, dt, x, wg, logits);
-    oracle_route(T, E, k, logits, bias, renormalize, ids, w, NULL);
+    oracle_route(T, E, k, logits, bias, renormalize, bias_mode, ids, w, NULL);
     int64_t n_dropped =
         oracle_permute(T, E, k, capacity, ids, NULL, raw, counts, offsets, row_token, pos, dropped);
 

@@ -47,16 +47,43 @@ int32_t oracle_capacity(int32_t T, int32_t k, int32_t E, double factor);
 void oracle_gate(int64_t T, int64_t H, int64_t E, int dt, const void* x, const void* wg,
                  float* logits);
 
+/* how a routing bias enters: added to the logits before the softmax (it changes
+ * the selection and the weights), or used to rank the experts only */
+enum { ORACLE_BIAS_SOFTMAX = 0, ORACLE_BIAS_SELECT = 1 };
+
 /* Softmax, top-k and renormalisation, [P3] §2.1; [P1] §2 (normalised weights).
  * keys l'[t,e] = logits[t,e] (+ bias[e] as one fp32 add when bias != NULL).
  * ids[t, 0..k-1]: the k experts with the largest key, largest first; equal keys
  * order by lower expert id (+0 and -0 are equal keys).
- * w[t,j]: softmax of the keys over all experts taken at ids[t,j]; with
- * renormalize != 0 divided by the sum of the k selected probabilities.
+ * w[t,j]: softmax over all experts taken at ids[t,j]; with renormalize != 0
+ * divided by the sum of the k selected probabilities.  The softmax is of the
+ * keys (bias_mode ORACLE_BIAS_SOFTMAX, the router sketch's comment: the bias is
+ * added to the logits) or of the logits alone (ORACLE_BIAS_SELECT: the bias
+ * ranks the experts and nothing else, the aux-free balancing of [P3] §2.1 and
+ * §4 read so that the bias steers load without changing the mixing weights).
  * margin[t] (optional): key of the k-th minus key of the (k+1)-th expert in
  * float64, +inf when k == E. */
 void oracle_route(int64_t T, int64_t E, int64_t k, const float* logits, const float* bias,
-                  int renormalize, int32_t* ids, double* w, double* margin);
+                  int renormalize, int bias_mode, int32_t* ids, double* w, double* margin);
+
+/* Routing load statistics and the next balancing bias.  [P1] §11 names the
+ * routing metrics to watch (variance of expert load, drop rate, how hot the
+ * hottest expert runs) and [P2] ("上线检查清单" / monitoring table) the token
+ * count of every expert and the skew of their distribution.
+ * raw[e]: slots (t, j) with ids[t,j] == e (ids outside [0, E) are not counted).
+ * ints[0..5]: picks = sum raw, dropped = sum max(0, raw[e] - capacity) (0 when
+ *   capacity < 0), max_count, hottest (lowest id with max_count), min_count,
+ *   idle (experts with raw == 0).
+ * reals[0..4]: mean = picks / E, stddev = sqrt(sum (raw[e] - mean)^2 / E)
+ *   (population), cv = stddev / mean, max_over_mean = max_count / mean (both 0
+ *   when mean == 0), drop_rate = dropped / picks (0 when picks == 0).
+ * bias_next[e] (optional, needs capacity >= 1): [P3] §2.1's aux-free update,
+ *   clamp(overflow / capacity, -1, 1) with overflow = raw[e] - capacity, taken
+ *   with the sign its comment states (an overloaded expert gets a negative
+ *   bias, which lowers its keys): clamp((capacity - raw[e]) / capacity, -1, 1),
+ *   computed in float64 and rounded once to fp32. */
+void oracle_load_stats(int64_t T, int64_t E, int64_t k, int32_t capacity, const int32_t* ids,
+                       int32_t* raw, int64_t* ints, double* reals, float* bias_next);
 
 /* Count, capacity drop, sort and pack, [P1] §8 (count, sort and pack by target
  * expert); [P3] §3.1 (grouping by expert id; per-expert buckets filled in
@@ -88,11 +115,12 @@ void oracle_combine(int64_t T, int64_t H, int64_t k, const double* yp, const int
                     const double* w, const double* ys, double* y);
 
 /* The whole layer on small inputs: gate, route, permute, per-expert FFN,
- * combine.  w1, w3 [E,I,H]; w2 [E,H,I]; ws1, ws3 [Is,H], ws2 [H,Is] or NULL
- * (Is = 0).  Optional outputs (NULL to skip): logits, ids, w, pos, counts.
+ * combine (bias_mode as in oracle_route).  w1, w3 [E,I,H]; w2 [E,H,I]; ws1,
+ * ws3 [Is,H], ws2 [H,Is] or NULL (Is = 0).  Optional outputs (NULL to skip): logits, ids, w, pos, counts.
  * Returns the number of dropped slots. */
 int64_t oracle_layer(int64_t T, int64_t H, int64_t E, int64_t k, int64_t I, int64_t Is,
-                     int32_t capacity, int renormalize, int dt, const void* x, const void* wg,
+                     int32_t capacity, int renormalize, int bias_mode, int dt, const void* x,
+                     const void* wg,
                      const float* bias, const void* w1, const void* w3, const void* w2,
                      const void* ws1, const void* ws3, const void* ws2, double* y,
                      float* logits_out, int32_t* ids_out, double* w_out, int32_t* pos_out,

@@ -3,7 +3,9 @@
 Each check compares the oracle with something other than itself: hand-derived
 closed forms (tests/golden/route_closed_forms.json), rank-counting brute force,
 NumPy's matrix product for the gate, SciPy's softmax for the k = E case, and
-the invariant that renormalised weights sum to one.
+the invariant that renormalised weights sum to one.  The selection-only bias
+is pinned by closed forms, by SciPy's softmax of the bare logits at k = E, and
+by the invariance of its weights to any bias that leaves the selection alone.
 """
 import json
 import math
@@ -25,7 +27,8 @@ def test_route_closed_forms():
     for c in cases:
         logits = np.array([[np.float32(float(v)) for v in c["logits"]]], np.float32)
         bias = np.array([np.float32(float(v)) for v in c["bias"]], np.float32) if "bias" in c else None
-        ids, w, _ = oracle.route(logits, c["k"], bias=bias, renormalize=c["renormalize"])
+        ids, w, _ = oracle.route(logits, c["k"], bias=bias, renormalize=c["renormalize"],
+                                 bias_mode=c.get("bias_mode", 0))
         assert ids[0].tolist() == c["ids"], c["name"]
         np.testing.assert_allclose(w[0], c["w"], rtol=0, atol=1e-7, err_msg=c["name"])
 
@@ -106,3 +109,33 @@ def test_bias_is_a_single_fp32_add():
     bias = np.array([0.0, 2.0 ** -23], np.float32)
     ids, _, _ = oracle.route(logits, 1, bias=bias)
     assert ids[0, 0] == 1
+
+
+@pytest.mark.parametrize("E", [2, 5, 16, 64])
+def test_selection_only_bias(E):
+    rng = np.random.default_rng(E)
+    logits = moe_synth.random_logits(seed=E + 5, T=40, E=E, ties=True)
+    bias = rng.standard_normal(E).astype(np.float32)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=-1)
+    for k in sorted({1, min(2, E), E}):
+        for renorm in (0, 1):
+            ids, w, margin = oracle.route(logits, k, bias=bias, renormalize=renorm, bias_mode=1)
+            ids0, _, margin0 = oracle.route(logits, k, bias=bias, renormalize=renorm, bias_mode=0)
+            # the selection (and its margin) is the biased one in both modes
+            assert np.array_equal(ids, ids0)
+            assert np.array_equal(margin, margin0, equal_nan=True)
+            for t in range(0, 40, 7):
+                assert ids[t].tolist() == route_by_rank(logits[t], k, bias)[0]
+            # the weights are the bare logits' softmax at the picked experts
+            pk = np.take_along_axis(p, ids.astype(np.int64), 1)
+            ref = pk / pk.sum(1, keepdims=True) if renorm else pk
+            np.testing.assert_allclose(w, ref, rtol=1e-12, atol=1e-15)
+    # a constant bias keeps the selection, so the weights equal the unbiased ones exactly
+    for k in sorted({1, min(3, E)}):
+        ids_c, w_c, _ = oracle.route(logits, k, bias=np.full(E, 0.5, np.float32), bias_mode=1)
+        ids_n, w_n, _ = oracle.route(logits, k)
+        assert np.array_equal(ids_c, ids_n) and np.array_equal(w_c, w_n)
+    # no bias: both modes are the plain router
+    a = oracle.route(logits, 1, bias_mode=1)
+    b = oracle.route(logits, 1)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
