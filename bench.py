@@ -35,6 +35,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--bias-mode", choices=("softmax", "select"), default="softmax",
+                    help="how a workload's routing bias enters: inside the softmax, or ranking only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -67,7 +69,7 @@ def main():
     t = workload_tensors(w, device=dev, log=log)
     cap = -1 if w.capacity_factor is None else moe.capacity(w.T, w.k, w.E, w.capacity_factor)
     d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, I_shared=w.I_shared, capacity=cap,
-                 renormalize=w.renormalize, dtype=w.dtype)
+                 renormalize=w.renormalize, dtype=w.dtype, bias_mode=args.bias_mode)
     ws = moe.workspace(d, dev)
     y = torch.empty((w.T, w.H), dtype=d.torch_dtype, device=dev)
     stream = torch.cuda.current_stream()
@@ -80,7 +82,8 @@ def main():
     # routing statistics (one extra untimed run)
     counts = torch.empty(w.E, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
-    step(dict(counts=counts, n_dropped=nd))
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    step(dict(counts=counts, n_dropped=nd, topk_ids=ids))
     torch.cuda.synchronize()
     cnt = counts.cpu().numpy().astype(np.int64)
     R = int(cnt.sum())
@@ -115,21 +118,34 @@ def main():
     stage_ms /= 5
     names = ["gate", "route", "permute", "gate_up", "down", "combine"]
 
+    # load statistics of this step's routing (moe_load_stats), values and launch time
+    st = moe.load_stats_buffer(dev)
+    e0, e1 = Event(), Event()
+    n_ls = 20
+    e0.record(sh)
+    for _ in range(n_ls):
+        moe.load_stats(d, ids, st, ws=ws)
+    e1.record(sh)
+    e1.synchronize()
+    load = {f: (round(v, 4) if isinstance(v, float) else v) for f, v in moe.read_load_stats(st).items()}
+    load["ms"] = round(e0.elapsed_ms(e1) / n_ls, 4)
+
     es = 2 if w.dtype == "bf16" else 4
     Is = w.I_shared
     F = 2.0 * w.T * w.H * w.E + 6.0 * R * w.H * w.I + 6.0 * w.T * w.H * Is
     B = (3.0 * w.H * w.I * es * touched + 3.0 * w.H * Is * es + w.E * w.H * es
          + 2.0 * w.T * w.H * es)
     gu_avg = float(np.mean(gu_ms))
-    decode = w.name == "dsv3_decode" or (R / max(touched, 1)) < 64
-    if decode:
-        # gate-up streams W1 and W3 of every touched expert (and the shared expert) once
-        gu_bytes = 2.0 * w.H * w.I * es * touched + 2.0 * w.H * Is * es + w.T * w.H * es
+    # the gate-up kernel's bound: whichever of its algorithmic flops at the MFMA peak and its
+    # algorithmic bytes (W1 and W3 of every touched expert and the shared expert, read once, and
+    # x) at the HBM peak takes longer
+    gu_bytes = 2.0 * w.H * w.I * es * touched + 2.0 * w.H * Is * es + w.T * w.H * es
+    gu_flops = 4.0 * R * w.H * w.I + 4.0 * w.T * w.H * Is
+    if gu_bytes / (PEAK_HBM_GBS * 1e9) > gu_flops / (PEAK_BF16_TFLOPS * 1e12):
         achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        gu_flops = 4.0 * R * w.H * w.I + 4.0 * w.T * w.H * Is
         achieved = gu_flops / (gu_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
@@ -160,13 +176,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded normal draws, shapes of the named workload)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
-                   "I_shared": Is, "capacity": cap, "accumulate": "fp32"},
+                   "I_shared": Is, "capacity": cap, "accumulate": "fp32",
+                   **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {})},
         "roofline": roof,
         "layer": {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
                   "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
                   "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
                   "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
-                  "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())]},
+                  "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
+                  "load_stats": load},
     }
 
     if not args.no_cpu_baseline:

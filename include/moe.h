@@ -63,6 +63,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  *  assignments dropped in token order (see moe_capacity).
  *  renormalize: 1 = divide the k picked probabilities by their sum ([P3]
  *  §2.1); 0 = keep the raw softmax probabilities.
+ *  bias_mode (moe_bias_mode_t): how a routing bias, when one is given, enters.
  *  Supported: bf16 needs H % 64 == 0, I % 64 == 0 and I_shared % 64 == 0;
  *  fp32 needs H % 4 == 0.  T * k must fit in int32. */
 typedef struct {
@@ -70,8 +71,35 @@ typedef struct {
   int32_t I_shared;
   int32_t capacity;
   int32_t renormalize;
-  int32_t dtype; /* moe_dtype_t */
+  int32_t dtype;     /* moe_dtype_t */
+  int32_t bias_mode; /* moe_bias_mode_t */
 } moe_dims_t;
+
+/* The per-expert routing bias of [P3] §2.1 (DeepSeek-V3's auxiliary-loss-free
+ * balancing) enters the router in one of two ways:
+ *  MOE_BIAS_SOFTMAX: added to the logits before the softmax, so it moves both
+ *    the selection and the weights (the reading of the router sketch's comment
+ *    that the bias is added to the logits);
+ *  MOE_BIAS_SELECT: added to the logits only to rank the experts; the weights
+ *    are the softmax of the logits without it, so the bias steers load without
+ *    changing how the picked experts are mixed. */
+typedef enum { MOE_BIAS_SOFTMAX = 0, MOE_BIAS_SELECT = 1 } moe_bias_mode_t;
+
+/* Load statistics of one routing decision, written by moe_load_stats into
+ * device memory.  "Picks" are the (token, slot) pairs whose id is in [0, E). */
+typedef struct {
+  int32_t picks;       /* sum of the per-expert pick counts                        */
+  int32_t dropped;     /* picks beyond an expert's capacity (0 when unlimited)      */
+  int32_t max_count;   /* most picks of one expert                                  */
+  int32_t hottest;     /* the expert with max_count (the lowest id among equals)    */
+  int32_t min_count;   /* fewest picks of one expert                                */
+  int32_t idle;        /* experts with no pick                                      */
+  float mean;          /* picks / E                                                 */
+  float stddev;        /* population standard deviation of the per-expert picks     */
+  float cv;            /* stddev / mean (0 when mean == 0)                          */
+  float max_over_mean; /* max_count / mean (0 when mean == 0)                       */
+  float drop_rate;     /* dropped / picks (0 when picks == 0)                       */
+} moe_load_stats_t;
 
 /* Stage boundaries of moe_layer_forward at which events can be recorded. */
 enum {
@@ -121,12 +149,13 @@ moe_status_t moe_gate(const moe_dims_t* dims, const void* x, const void* wg, flo
                       void* stream);
 
 /* Softmax, top-k, renormalisation and capacity drop, [P3] §2.1.
- *  logits [T,E] fp32; bias [E] fp32 or NULL, added to the logits (one fp32
- *  add) before the softmax and the selection.
+ *  logits [T,E] fp32; bias [E] fp32 or NULL.  The selection keys are
+ *  logits + bias (one fp32 add).
  *  topk_ids [T,k]: the k experts with the largest key, largest first; equal
  *  keys (+0 == -0) go to the lower expert id.
  *  topk_w [T,k]: their softmax probabilities, renormalised over the k picks
- *  when dims->renormalize.
+ *  when dims->renormalize; the softmax is of the keys (MOE_BIAS_SOFTMAX) or
+ *  of the logits alone (MOE_BIAS_SELECT).
  *  counts [E] (or NULL): rows each expert keeps after the capacity drop.
  *  dropped [T,k] u8 (or NULL): 1 where the slot was dropped (capacity reached
  *  by earlier tokens of that expert).  n_dropped [1] (or NULL).
@@ -172,11 +201,30 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, const void* x_packed, const 
 moe_status_t moe_combine(const moe_dims_t* dims, const void* y_packed, const int32_t* pos,
                          const float* topk_w, const void* y_shared, void* y, void* stream);
 
+/* Routing load statistics, the routing metrics [P1] §11 names (variance of
+ * expert load, drop rate, how hot the hottest expert runs) and the per-expert
+ * token counts and skew of [P2]'s monitoring table; with bias_next, also the
+ * next value of [P3] §2.1's auxiliary-loss-free balancing bias.
+ *  topk_ids [T,k] (as moe_route writes them); ids outside [0, E) are ignored.
+ *  raw_counts [E] or NULL: picks of each expert before the capacity.
+ *  stats [1] (device): see moe_load_stats_t; dropped uses dims->capacity.
+ *  bias_next [E] or NULL: clamp((C - raw[e]) / C, -1, 1) with C =
+ *  dims->capacity, computed in fp64 and rounded once: the page's
+ *  clamp(overflow / capacity, -1, 1), overflow = picks - capacity, with the
+ *  sign its comment states (an overloaded expert gets a negative bias, which
+ *  lowers its keys).  Needs dims->capacity >= 1, else MOE_ERR_INVALID_ARG.
+ *  Needs the workspace.  Integer outputs are exact; the float statistics are
+ *  computed in fp64 with a fixed summation order and rounded once. */
+moe_status_t moe_load_stats(const moe_dims_t* dims, const int32_t* topk_ids, int32_t* raw_counts,
+                            moe_load_stats_t* stats, float* bias_next, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* The whole layer in one enqueue: gate, route (+bias, capacity), permute,
  * grouped gate-up with SiLU*mul, grouped down, combine.  The pack is fused into
  * the gate-up GEMM's row loads.  The shared expert (dims->I_shared > 0) runs
  * as one more group over all T tokens.
- *  x [T,H], wg [E,H], bias [E] fp32 or NULL, w1/w3 [E,I,H], w2 [E,H,I],
+ *  x [T,H], wg [E,H], bias [E] fp32 or NULL (entering as dims->bias_mode
+ *  says), w1/w3 [E,I,H], w2 [E,H,I],
  *  ws1/ws3 [I_shared,H], ws2 [H,I_shared] (NULL when I_shared == 0), y [T,H].
  *  dbg: NULL, or a struct whose non-NULL members receive intermediates. */
 moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg,

@@ -5,5 +5,5 @@ thin torch binding.  Submodules load the library on first use and raise when it
 has not been built.
 """
 from ._lib import LIB_PATH, MoeError, EXPORTS  # noqa: F401
-from .api import (Dims, capacity, combine, expert_ffn, gate, layer_forward, permute,  # noqa: F401
-                  route, workspace, workspace_bytes)
+from .api import (Dims, capacity, combine, expert_ffn, gate, layer_forward, load_stats,  # noqa: F401
+                  load_stats_buffer, permute, read_load_stats, route, workspace, workspace_bytes)

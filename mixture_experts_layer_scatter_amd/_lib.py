@@ -13,13 +13,21 @@ MOE_F32, MOE_BF16 = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_capacity", "moe_workspace_bytes", "moe_gate", "moe_route",
-           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_load_stats", "moe_layer_forward")
+MOE_BIAS_SOFTMAX, MOE_BIAS_SELECT = 0, 1
 
 
 class MoeDims(C.Structure):
     _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("I", C.c_int32), ("I_shared", C.c_int32), ("capacity", C.c_int32),
-                ("renormalize", C.c_int32), ("dtype", C.c_int32)]
+                ("renormalize", C.c_int32), ("dtype", C.c_int32), ("bias_mode", C.c_int32)]
+
+
+class MoeLoadStats(C.Structure):
+    _fields_ = [("picks", C.c_int32), ("dropped", C.c_int32), ("max_count", C.c_int32),
+                ("hottest", C.c_int32), ("min_count", C.c_int32), ("idle", C.c_int32),
+                ("mean", C.c_float), ("stddev", C.c_float), ("cv", C.c_float),
+                ("max_over_mean", C.c_float), ("drop_rate", C.c_float)]
 
 
 class MoeDebugOut(C.Structure):
@@ -66,6 +74,8 @@ def lib():
         L.moe_expert_ffn.argtypes = [D, p, p, p, p, p, p, p, sz, p]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [D, p, p, p, p, p, p]
+        L.moe_load_stats.restype = i32
+        L.moe_load_stats.argtypes = [D, p, p, p, p, p, sz, p]
         L.moe_layer_forward.restype = i32
         L.moe_layer_forward.argtypes = [D, p, p, p, p, p, p, p, p, p, p, C.POINTER(MoeDebugOut), p,
                                         sz, p]

@@ -13,9 +13,10 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeDebugOut, MoeDims, MoeError
+from ._lib import MoeDebugOut, MoeDims, MoeError, MoeLoadStats
 
 _DT = {"bf16": _lib.MOE_BF16, "f32": _lib.MOE_F32}
+_BIAS = {"softmax": _lib.MOE_BIAS_SOFTMAX, "select": _lib.MOE_BIAS_SELECT}
 _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
@@ -30,10 +31,11 @@ class Dims:
     capacity: int = -1
     renormalize: int = 1
     dtype: str = "bf16"
+    bias_mode: str = "softmax"  # "softmax": bias inside the softmax; "select": ranking only
 
     def c(self) -> MoeDims:
         return MoeDims(self.T, self.H, self.E, self.k, self.I, self.I_shared, self.capacity,
-                       self.renormalize, _DT[self.dtype])
+                       self.renormalize, _DT[self.dtype], _BIAS[self.bias_mode])
 
     @property
     def torch_dtype(self):
@@ -125,6 +127,33 @@ def combine(d: Dims, y_packed, pos, w, y_shared, y, stream=None):
         C.byref(c), _ptr(y_packed, dt, "y_packed"), _ptr(pos, torch.int32, "pos"),
         _ptr(w, torch.float32, "w"), _ptr(y_shared, dt, "y_shared"), _ptr(y, dt, "y"),
         _stream(stream)), "moe_combine")
+
+
+# fields of moe_load_stats_t, in order
+LOAD_STATS_FIELDS = tuple(f for f, _ in MoeLoadStats._fields_)
+
+
+def load_stats_buffer(device="cuda") -> torch.Tensor:
+    """Device bytes for one moe_load_stats_t."""
+    return torch.zeros(C.sizeof(MoeLoadStats), dtype=torch.uint8, device=device)
+
+
+def read_load_stats(buf: torch.Tensor) -> dict:
+    """Host copy of a moe_load_stats_t written by load_stats (synchronises)."""
+    raw = bytes(buf.cpu().numpy().tobytes())
+    s = MoeLoadStats.from_buffer_copy(raw)
+    return {f: getattr(s, f) for f in LOAD_STATS_FIELDS}
+
+
+def load_stats(d: Dims, ids, stats, raw_counts=None, bias_next=None, ws=None, stream=None):
+    """Per-expert picks, load statistics into `stats` (load_stats_buffer) and, optionally, the
+    next balancing bias."""
+    c = d.c()
+    _check(_lib.lib().moe_load_stats(
+        C.byref(c), _ptr(ids, torch.int32, "ids"), _ptr(raw_counts, torch.int32, "raw_counts"),
+        _ptr(stats, torch.uint8, "stats"), _ptr(bias_next, torch.float32, "bias_next"),
+        _ptr(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)),
+        "moe_load_stats")
 
 
 def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None, debug=None,

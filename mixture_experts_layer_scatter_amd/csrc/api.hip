@@ -91,6 +91,7 @@ moe_status_t check_dims(const moe_dims_t* d) {
   if (d->k < 1 || d->k > d->E) return MOE_ERR_INVALID_ARG;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (d->bias_mode != MOE_BIAS_SOFTMAX && d->bias_mode != MOE_BIAS_SELECT) return MOE_ERR_INVALID_ARG;
   if (d->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->T * d->k > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_BF16) {
@@ -304,7 +305,8 @@ moe_status_t moe_route(const moe_dims_t* d, const float* logits, const float* bi
   if (need_ws && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (d->T > 0)
-    MOE_TRY(launch_route(logits, bias, d->T, d->E, d->k, d->renormalize, topk_ids, topk_w, s));
+    MOE_TRY(launch_route(logits, bias, d->T, d->E, d->k, d->renormalize, d->bias_mode, topk_ids,
+                         topk_w, s));
   if (!need_ws) return MOE_OK;
   PermuteArgs a = permute_args(d, L, ws);
   a.ids = topk_ids;
@@ -313,6 +315,26 @@ moe_status_t moe_route(const moe_dims_t* d, const float* logits, const float* bi
   if (n_dropped) a.n_dropped = n_dropped;
   a.dropped = dropped;
   MOE_TRY(launch_permute(a, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_load_stats(const moe_dims_t* d, const int32_t* topk_ids, int32_t* raw_counts,
+                            moe_load_stats_t* stats, float* bias_next, void* ws, size_t ws_bytes,
+                            void* stream) {
+  moe_status_t st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!stats || (d->T > 0 && !topk_ids)) return MOE_ERR_INVALID_ARG;
+  if (bias_next && d->capacity < 1) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  // the permutation's histogram and scan give the per-expert picks (no rows are placed)
+  PermuteArgs a = permute_args(d, L, ws);
+  a.ids = topk_ids;
+  a.capacity = d->capacity;
+  if (raw_counts) a.raw = raw_counts;
+  MOE_TRY(launch_permute(a, s));
+  MOE_TRY(launch_load_stats(a.raw, d->E, d->capacity, stats, bias_next, s));
   return MOE_OK;
 }
 
@@ -400,7 +422,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
   MOE_TRY(mark(ev, MOE_EV_START, s));
   MOE_TRY(run_gate(d, x, wg, logits, s, gate_splits(d), at<float>(ws, L.gate_part)));
   MOE_TRY(mark(ev, MOE_EV_GATE, s));
-  MOE_TRY(launch_route(logits, bias, T, E, k, d->renormalize, ids, w, s));
+  MOE_TRY(launch_route(logits, bias, T, E, k, d->renormalize, d->bias_mode, ids, w, s));
   MOE_TRY(mark(ev, MOE_EV_ROUTE, s));
   // 3. count, capacity, scan, stable scatter (rows of the folded shared expert appended)
   PermuteArgs a = permute_args(d, L, ws);

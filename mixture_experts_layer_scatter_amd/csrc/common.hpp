@@ -36,7 +36,12 @@ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // route.hip: one wavefront per token; softmax, top-k, renormalise.
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
-                        int renormalize, int32_t* ids, float* w, hipStream_t s);
+                        int renormalize, int bias_mode, int32_t* ids, float* w, hipStream_t s);
+
+// stats.hip: load statistics of the per-expert pick counts (raw, after launch_permute's scan)
+// and the next balancing bias
+hipError_t launch_load_stats(const int32_t* raw, int E, int capacity, void* stats,
+                             float* bias_next, hipStream_t s);
 
 // permute.hip
 struct PermuteArgs {

@@ -11,6 +11,11 @@
 // ascending among equal keys, with +0 and -0 equal.  Each lane keeps EPL keys
 // in registers; k rounds of a wavefront max over a 64-bit (key, ~id) word pick
 // the experts in slot order.
+//
+// The bias of the same §2.1 (auxiliary-loss-free balancing) either sits inside
+// the softmax (the weights are those of the keys) or only ranks the experts
+// (the weights are those of the bare logits, so it steers load without
+// changing how the picked experts are mixed).
 #include "common.hpp"
 
 namespace moe {
@@ -33,6 +38,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
   // butterfly: every lane ends with the same, order-fixed sum
 #pragma unroll
@@ -43,7 +54,7 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
-                                                    int k, int renormalize,
+                                                    int k, int renormalize, int sel_only,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -51,17 +62,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   if (t >= T) return;  // whole wavefront leaves together
   const float* row = logits + (int64_t)t * E;
 
-  float key[EPL];
+  // key: what the experts are ranked by; val: what the softmax is taken of
+  float key[EPL], val[EPL];
   bool taken[EPL];
 #pragma unroll
   for (int s = 0; s < EPL; ++s) {
     const int e = s * kWave + lane;
-    float v = -INFINITY;
+    float v = -INFINITY, l = -INFINITY;
     if (e < E) {
-      v = row[e];
-      if (bias) v = v + bias[e];  // one fp32 add
+      l = row[e];
+      v = bias ? l + bias[e] : l;  // one fp32 add
     }
     key[s] = v;
+    val[s] = sel_only ? l : v;
     taken[s] = e >= E;
   }
 
@@ -86,13 +99,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     best = wave_max_u64(best);
     const int e = (int)(~(uint32_t)best);
-    // the owner lane marks it and reports the exact key value
+    // the owner lane marks it and reports its softmax value
     float v = 0.f;
 #pragma unroll
     for (int s = 0; s < EPL; ++s) {
       if (s * kWave + lane == e) {
         taken[s] = true;
-        v = key[s];
+        v = val[s];
       }
     }
     v = __shfl(v, e & (kWave - 1), kWave);
@@ -106,7 +119,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
   }
 
-  // weights: exp(key - max) over the picked experts, divided by the picked sum
+  // the shift of the exponentials: the first pick's value is the largest of the row when the
+  // softmax is of the keys; of the bare logits, take the picked maximum (renormalised) or the
+  // row maximum (raw probabilities), so that the largest term is exp(0)
+  if (sel_only) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) {
+      const int i = s * kWave + lane;
+      if (renormalize ? i < k : i < E) m = fmaxf(m, renormalize ? selv[s] : val[s]);
+    }
+    top = wave_max_f32(m);
+  }
+  // weights: exp(value - shift) over the picked experts, divided by the picked sum
   // (renormalised) or by the sum over every expert (raw softmax probability)
   float ex[EPL];
   float part = 0.f;
@@ -121,7 +146,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   } else {
 #pragma unroll
     for (int s = 0; s < EPL; ++s)
-      if (s * kWave + lane < E) part += expf(key[s] - top);
+      if (s * kWave + lane < E) part += expf(val[s] - top);
   }
   const float denom = wave_sum_f32(part);
 #pragma unroll
@@ -135,21 +160,22 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
-                        int renormalize, int32_t* ids, float* w, hipStream_t s) {
+                        int renormalize, int bias_mode, int32_t* ids, float* w, hipStream_t s) {
+  const int sel = bias != nullptr && bias_mode == 1;
   if (T <= 0) return hipSuccess;
   const int per_block = 4;  // tokens (wavefronts) per block
   dim3 grid(ceil_div(T, per_block)), block(per_block * kWave);
   const int epl = ceil_div(E, kWave);
   if (epl <= 1)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, ids, w);
+    route_kernel<1><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
   else if (epl <= 2)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, ids, w);
+    route_kernel<2><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
   else if (epl <= 4)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, ids, w);
+    route_kernel<4><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
   else if (epl <= 8)
-    route_kernel<8><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, ids, w);
+    route_kernel<8><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
   else
-    route_kernel<16><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, ids, w);
+    route_kernel<16><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
   return hipGetLastError();
 }
 

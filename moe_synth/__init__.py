@@ -49,6 +49,7 @@ class Workload:
     capacity_factor: float | None = None  # None = unlimited
     zipf_s: float | None = None           # per-expert logit bias exponent, None = no bias
     renormalize: int = 1
+    bias_mode: int = 0  # 0: the bias enters the softmax; 1: it only ranks the experts
 
     @property
     def seed(self) -> int:

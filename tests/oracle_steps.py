@@ -33,7 +33,8 @@ def routing(w: moe_synth.Workload, x=None, logits=None):
     if logits is None:
         logits = oracle.gate(x, moe_synth.gate_weight(w))
     bias = moe_synth.logit_bias(w)
-    ids, wts, margin = oracle.route(logits, w.k, bias=bias, renormalize=w.renormalize)
+    ids, wts, margin = oracle.route(logits, w.k, bias=bias, renormalize=w.renormalize,
+                                    bias_mode=w.bias_mode)
     cap = oracle.capacity(logits.shape[0], w.k, w.E, w.capacity_factor)
     perm = oracle.permute(ids, w.E, cap)
     return dict(logits=logits, ids=ids, w=wts, margin=margin, capacity=cap, **perm)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 def _dims(**kw):
     L = _lib()
     base = dict(T=16, H=128, E=8, k=2, I=128, I_shared=0, capacity=-1, renormalize=1,
-                dtype=L.MOE_BF16)
+                dtype=L.MOE_BF16, bias_mode=L.MOE_BIAS_SOFTMAX)
     base.update(kw)
     return L.MoeDims(**base)
 
@@ -59,7 +59,8 @@ def test_workspace_bytes():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k=0), 1), (dict(k=9), 1), (dict(T=-1), 1), (dict(E=0), 1), (dict(dtype=7), 1),
-    (dict(renormalize=2), 1), (dict(E=2048, k=2), 2), (dict(H=100), 2), (dict(I=96), 2),
+    (dict(renormalize=2), 1), (dict(bias_mode=2), 1), (dict(bias_mode=-1), 1),
+    (dict(E=2048, k=2), 2), (dict(H=100), 2), (dict(I=96), 2),
     (dict(I_shared=32), 2), (dict(H=6, dtype=0), 2),
 ])
 def test_bad_dims_rejected_before_launch(kw, status):
@@ -106,3 +107,46 @@ def test_zero_tokens_is_a_noop():
     p = C.c_void_p(16)
     assert lib.moe_layer_forward(C.byref(d), None, None, None, None, None, None, None, None, None,
                                  None, None, p, need, None) == L.MOE_OK
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors have the header's field offsets and sizes (a C program built with gcc
+    against include/moe.h prints them)."""
+    import subprocess
+    L = _lib()
+    src = tmp_path / "layout.c"
+    fields = {"moe_dims_t": [f for f, _ in L.MoeDims._fields_],
+              "moe_load_stats_t": [f for f, _ in L.MoeLoadStats._fields_],
+              "moe_debug_out_t": [f for f, _ in L.MoeDebugOut._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'printf("{st} size %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for st, cls in (("moe_dims_t", L.MoeDims), ("moe_load_stats_t", L.MoeLoadStats),
+                    ("moe_debug_out_t", L.MoeDebugOut)):
+        assert got[(st, "size")] == C.sizeof(cls), st
+        for f in fields[st]:
+            assert got[(st, f)] == getattr(cls, f).offset, (st, f)
+
+
+def test_load_stats_argument_checks():
+    L = _lib()
+    lib = L.lib()
+    p = C.c_void_p(16)  # never dereferenced
+    d = _dims(capacity=-1)
+    # no stats pointer, no ids with tokens, a bias update without a capacity, no workspace
+    assert lib.moe_load_stats(C.byref(d), p, None, None, None, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(C.byref(d), None, None, p, None, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(C.byref(d), p, None, p, p, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    d0 = _dims(capacity=0)
+    assert lib.moe_load_stats(C.byref(d0), p, None, p, p, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_stats(C.byref(d), p, None, p, None, None, 0, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_load_stats(C.byref(d), p, None, p, None, p, 16, None) == L.MOE_ERR_WORKSPACE

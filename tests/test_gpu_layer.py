@@ -30,7 +30,8 @@ import mixture_experts_layer_scatter_amd as moe
 def run_gpu(w, t):
     cap = -1 if w.capacity_factor is None else moe.capacity(w.T, w.k, w.E, w.capacity_factor)
     d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, I_shared=w.I_shared, capacity=cap,
-                 renormalize=w.renormalize, dtype=w.dtype)
+                 renormalize=w.renormalize, dtype=w.dtype,
+                 bias_mode=("softmax", "select")[w.bias_mode])
     dbg = dict(logits=torch.empty((w.T, w.E), dtype=torch.float32, device="cuda"),
                topk_ids=torch.empty((w.T, w.k), dtype=torch.int32, device="cuda"),
                topk_w=torch.empty((w.T, w.k), dtype=torch.float32, device="cuda"),
@@ -117,6 +118,16 @@ def test_full_size_sampled_tokens(name, n):
     check_layer(moe_synth.get(name), n_sample=n, seed=1)
 
 
+@pytest.mark.parametrize("T", [640, 2048])
+def test_selection_only_bias_every_token(T):
+    """The skewed workload with its Zipf bias used for ranking only (weights from the bare
+    logits), reduced in T, every token checked."""
+    need_gpu()
+    import dataclasses
+    w = dataclasses.replace(moe_synth.get("skewed_capacity").scaled(T), bias_mode=1)
+    check_layer(w)
+
+
 def test_deterministic():
     need_gpu()
     w = moe_synth.get("qwen3_prefill").scaled(512)
@@ -145,13 +156,14 @@ def _random_workloads(n=14, seed=2024):
         T = int(rng.choice([1, 7, 100, 333, 1000]))
         out.append(moe_synth.Workload(f"random{i}", 100 + i, T=T, H=H, E=E, k=k, I=I,
                                       I_shared=shared, dtype=dtype, capacity_factor=cf,
-                                      zipf_s=zipf, renormalize=int(rng.random() < 0.8)))
+                                      zipf_s=zipf, renormalize=int(rng.random() < 0.8),
+                                      bias_mode=i % 2 if zipf else 0))
     return out
 
 
 @pytest.mark.parametrize("w", _random_workloads(), ids=lambda w: (
     f"{w.name}-{w.dtype}-T{w.T}-H{w.H}-E{w.E}-k{w.k}-I{w.I}-Is{w.I_shared}-cf{w.capacity_factor}"
-    f"-z{w.zipf_s}-r{w.renormalize}"))
+    f"-z{w.zipf_s}-r{w.renormalize}-b{w.bias_mode}"))
 def test_random_shapes_every_token(w):
     need_gpu()
     check_layer(w)

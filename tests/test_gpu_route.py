@@ -17,9 +17,10 @@ pytestmark = pytest.mark.gpu
 import mixture_experts_layer_scatter_amd as moe
 
 
-def _run(logits, k, bias=None, renorm=1, capacity=-1):
+def _run(logits, k, bias=None, renorm=1, capacity=-1, bias_mode=0):
     T, E = logits.shape
-    d = moe.Dims(T=T, H=64, E=E, k=k, I=64, capacity=capacity, renormalize=renorm)
+    d = moe.Dims(T=T, H=64, E=E, k=k, I=64, capacity=capacity, renormalize=renorm,
+                 bias_mode=("softmax", "select")[bias_mode])
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
@@ -31,10 +32,10 @@ def _run(logits, k, bias=None, renorm=1, capacity=-1):
     return ids.cpu().numpy(), w.cpu().numpy(), counts.cpu().numpy(), dropped.cpu().numpy(), int(nd.item())
 
 
-def _check(logits, k, bias=None, renorm=1, capacity=-1):
+def _check(logits, k, bias=None, renorm=1, capacity=-1, bias_mode=0):
     T, E = logits.shape
-    ids, w, counts, dropped, nd = _run(logits, k, bias, renorm, capacity)
-    oids, ow, _ = oracle.route(logits, k, bias=bias, renormalize=renorm)
+    ids, w, counts, dropped, nd = _run(logits, k, bias, renorm, capacity, bias_mode)
+    oids, ow, _ = oracle.route(logits, k, bias=bias, renormalize=renorm, bias_mode=bias_mode)
     assert np.array_equal(ids, oids), f"ids differ at {np.argwhere(ids != oids)[:5].tolist()}"
     assert np.abs(w - ow).max() <= 1e-6
     p = oracle.permute(oids, E, capacity)
@@ -56,6 +57,20 @@ def test_route_bit_exact_with_ties(E, k, renorm):
         if E % 2 == 0:
             bias = np.random.default_rng(E).standard_normal(E).astype(np.float32)
         _check(logits, k, bias, renorm)
+
+
+@pytest.mark.parametrize("E,k", [(2, 1), (8, 2), (64, 6), (256, 8), (1024, 16), (100, 100)])
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_route_selection_only_bias(E, k, renorm):
+    """The bias ranks the experts; the weights are the bare logits' softmax.  Strong biases
+    pick experts whose logits sit far below the row maximum."""
+    need_gpu()
+    log(f"route selection-only bias E={E} k={k} renorm={renorm}")
+    rng = np.random.default_rng(E * 3 + k)
+    for T, scale in ((1, 1.0), (300, 0.5), (2000, 8.0)):
+        logits = moe_synth.random_logits(seed=E + k + T, T=T, E=E, ties=True)
+        bias = (scale * rng.standard_normal(E)).astype(np.float32)
+        _check(logits, k, bias, renorm, capacity=max(1, T * k // E), bias_mode=1)
 
 
 @pytest.mark.parametrize("cap", [0, 1, 3, 50, 10 ** 6])
