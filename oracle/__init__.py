@@ -18,7 +18,7 @@ from . import build as _build
 
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 _p = C.c_void_p
 _i64 = C.c_int64
@@ -39,6 +39,14 @@ def lib():
         L.oracle_gate.argtypes = [_i64, _i64, _i64, C.c_int, _p, _p, _p]
         L.oracle_route.restype = None
         L.oracle_route.argtypes = [_i64, _i64, _i64, _p, _p, C.c_int, C.c_int, _p, _p, _p]
+        L.oracle_fp8_decode.restype = C.c_double
+        L.oracle_fp8_decode.argtypes = [C.c_uint8]
+        L.oracle_fp8_encode.restype = C.c_uint8
+        L.oracle_fp8_encode.argtypes = [C.c_float]
+        L.oracle_quantize_fp8.restype = None
+        L.oracle_quantize_fp8.argtypes = [_i64, _i64, C.c_int, _p, _p, _p]
+        L.oracle_dequantize_fp8.restype = None
+        L.oracle_dequantize_fp8.argtypes = [_i64, _i64, _p, _p, _p]
         L.oracle_load_stats.restype = None
         L.oracle_load_stats.argtypes = [_i64, _i64, _i64, _i32, _p, _p, _p, _p, _p]
         L.oracle_permute.restype = _i64
@@ -58,7 +66,9 @@ def _dt(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle inputs are bf16 bits (uint16) or float32, got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are bf16 bits (uint16), float32 or float64, got {a.dtype}")
 
 
 def _ptr(a):
@@ -147,6 +157,35 @@ def permute(ids: np.ndarray, E: int, capacity: int = -1, active: np.ndarray | No
     R = int(offsets[E])
     return dict(raw=raw, counts=counts, offsets=offsets, row_token=row_token[:R], pos=pos,
                 dropped=dropped, n_dropped=int(nd))
+
+
+def fp8_decode(code: int) -> float:
+    return float(lib().oracle_fp8_decode(int(code)))
+
+
+def fp8_encode(x: float) -> int:
+    return int(lib().oracle_fp8_encode(float(x)))
+
+
+def quantize_fp8(w: np.ndarray):
+    """Per-row FP8 E4M3 quantisation of a [rows, K] bf16-bits or float32 matrix (any leading
+    shape is flattened into rows).  Returns (codes uint8, same shape; scales float32 [rows])."""
+    w = _c(w)
+    K = w.shape[-1]
+    rows = w.size // K if K else 0
+    q = np.empty(w.shape, np.uint8)
+    sc = np.empty(w.shape[:-1], np.float32)
+    lib().oracle_quantize_fp8(rows, K, _dt(w), _ptr(w), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def dequantize_fp8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.float32)
+    K = q.shape[-1]
+    out = np.empty(q.shape, np.float64)
+    lib().oracle_dequantize_fp8(q.size // K if K else 0, K, _ptr(q), _ptr(scales), _ptr(out))
+    return out
 
 
 def expert_ffn(xr: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:

@@ -16,7 +16,7 @@
 
 int oracle_threads(void) { return omp_get_max_threads(); }
 
-/* exact float64 value of element i of a bf16 or fp32 tensor */
+/* exact float64 value of element i of a bf16, fp32 or float64 tensor */
 static double ld(int dt, const void* p, int64_t i) {
     if (dt == ORACLE_BF16) {
         uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
@@ -24,7 +24,65 @@ static double ld(int dt, const void* p, int64_t i) {
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dt == ORACLE_F64) return ((const double*)p)[i];
     return (double)((const float*)p)[i];
+}
+
+double oracle_fp8_decode(uint8_t c) {
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    /* subnormal: m/8 * 2^(1-7); normal: (1 + m/8) * 2^(e-7) */
+    double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+uint8_t oracle_fp8_encode(float x) {
+    if (isnan(x)) return 0x7f;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs((double)x);
+    if (a >= 448.0) return sign | 0x7e; /* saturate (448 is the largest finite value) */
+    /* the quantum at a's binade: 2^(E-3) for a normal a in [2^E, 2^(E+1)), E >= -6; 2^-9 below */
+    int E;
+    frexp(a, &E); /* a = f * 2^E with f in [0.5, 1): the binade is [2^(E-1), 2^E) */
+    E -= 1;
+    if (E < -6) E = -6;
+    double quantum = ldexp(1.0, E - 3);
+    double n = nearbyint(a / quantum); /* a / quantum is exact; ties to even (default mode) */
+    double v = n * quantum;             /* may step up into the next binade: still exact */
+    /* encode v: find its exponent field and mantissa */
+    if (v == 0.0) return sign;
+    int Ev;
+    frexp(v, &Ev);
+    Ev -= 1;
+    if (Ev < -6) return sign | (uint8_t)(v / ldexp(1.0, -9)); /* subnormal: m = v / 2^-9 */
+    uint8_t m = (uint8_t)(v / ldexp(1.0, Ev - 3) - 8.0);
+    return sign | (uint8_t)((Ev + 7) << 3) | m;
+}
+
+void oracle_quantize_fp8(int64_t rows, int64_t K, int dt, const void* w, uint8_t* q,
+                         float* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = (float)fabs(ld(dt, w, r * K + k)); /* bf16 and fp32 values are exact */
+            if (a > amax) amax = a;
+        }
+        float scale = amax / 448.0f;
+        scales[r] = scale;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)ld(dt, w, r * K + k);
+            q[r * K + k] = scale == 0.0f ? 0 : oracle_fp8_encode(v / scale);
+        }
+    }
+}
+
+void oracle_dequantize_fp8(int64_t rows, int64_t K, const uint8_t* q, const float* scales,
+                           double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = oracle_fp8_decode(q[r * K + k]) * (double)scales[r];
 }
 
 int32_t oracle_capacity(int32_t T, int32_t k, int32_t E, double factor) {

@@ -34,8 +34,31 @@ extern "C" {
 /* OpenMP threads the parallel outer loops use */
 int oracle_threads(void);
 
-/* storage type of a tensor argument */
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+/* storage type of a tensor argument (F64: plain doubles, e.g. dequantised weights) */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* FP8 E4M3 (the OCP "E4M3FN" format: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, no infinities, S.1111.111 is NaN, largest finite 448).
+ * fp8_decode: the exact value of a code.
+ * fp8_encode: the code nearest to x, ties to the even code (the one whose mantissa is even),
+ * |x| > 448 saturating to +-448; NaN gives 0x7f.  Written from the format's definition. */
+double oracle_fp8_decode(uint8_t code);
+uint8_t oracle_fp8_encode(float x);
+
+/* Weight-only FP8 quantisation of a [rows, K] matrix, one scale per row (per output
+ * channel of a linear layer's [out, in] weight).  The pages name 8-bit quantisation of expert
+ * weights for the serving configuration ([P3] §5.2, "w4afp8": 4-bit weights, FP8
+ * activations); reading: FP8 weights with per-row fp32 scales, activations kept in bf16.
+ *   amax[r]  = max_k |w[r,k]|;
+ *   scale[r] = fp32(amax[r] / 448)  (one correctly rounded fp32 division);
+ *   q[r,k]   = fp8_encode(fp32(w[r,k] / scale[r]))  (fp32 division), 0 when scale[r] == 0.
+ * The dequantised weight is fp8_decode(q[r,k]) * scale[r]. */
+void oracle_quantize_fp8(int64_t rows, int64_t K, int dt, const void* w, uint8_t* q,
+                         float* scales);
+
+/* out[r,k] = fp8_decode(q[r,k]) * scales[r], exact in float64. */
+void oracle_dequantize_fp8(int64_t rows, int64_t K, const uint8_t* q, const float* scales,
+                           double* out);
 
 /* Expert capacity, [P3] §2.1 (router sketch, capacity = tokens / experts x
  * factor), with the top-k factor included: floor(T*k/E*factor) in double. */
@@ -102,7 +125,8 @@ int64_t oracle_permute(int64_t T, int64_t E, int64_t k, int32_t capacity, const 
 /* One expert's SwiGLU FFN on M rows, [P1] §1 (FFN(x) = W2 s(W1 x) with an added
  * gate projection) and §2 (input and output of hidden size, inner size I):
  * out[m,:] = W2 ( silu(W1 x_m) * (W3 x_m) ), silu(a) = a / (1 + exp(-a)).
- * xr [M,H] storage `dt_x`; w1, w3 [I,H] and w2 [H,I] storage `dt_w`;
+ * xr [M,H] storage `dt_x`; w1, w3 [I,H] and w2 [H,I] storage `dt_w` (ORACLE_F64 for
+ * dequantised FP8 weights);
  * out [M,H] float64. */
 void oracle_expert_ffn(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr, int dt_w,
                        const void* w1, const void* w3, const void* w2, double* out);

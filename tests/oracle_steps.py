@@ -28,6 +28,24 @@ class Weights:
         return t
 
 
+class Fp8Weights(Weights):
+    """The same experts quantised to FP8 E4M3 with per-row scales by the oracle, returned
+    dequantised (float64): the weights an FP8 layer computes with."""
+
+    def expert(self, e):
+        if e in self._e:
+            return self._e[e]
+        t = tuple(fp8_dequantised(a) for a in moe_synth.expert_weights(self.w, e))
+        if self.cache:
+            self._e[e] = t
+        return t
+
+
+def fp8_dequantised(a):
+    q, s = oracle.quantize_fp8(a)
+    return oracle.dequantize_fp8(q, s)
+
+
 def routing(w: moe_synth.Workload, x=None, logits=None):
     """Oracle gate (unless logits are given), route and permute for workload w."""
     if logits is None:
