@@ -35,6 +35,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--weights", choices=("same", "fp8"), default="same",
+                    help="expert weights in the layer's storage type, or FP8 E4M3 with per-row "
+                         "scales (quantised once before timing; bf16 layers)")
     ap.add_argument("--bias-mode", choices=("softmax", "select"), default="softmax",
                     help="how a workload's routing bias enters: inside the softmax, or ranking only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -75,9 +78,37 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    def step(debug=None):
+    fp8 = args.weights == "fp8"
+    quant_err = None
+    if fp8:
+        if w.dtype != "bf16":
+            sys.exit("--weights fp8 needs a bf16 workload")
+        # reference output with the bf16 weights, then quantise and drop them
         moe.layer_forward(d, t["x"], t["wg"], t["bias"], t["w1"], t["w3"], t["w2"], t["shared"],
-                          y=y, ws=ws, debug=debug)
+                          y=y, ws=ws)
+        y_ref = y.float().clone()
+        q = {k: moe.quantize_fp8(t[k]) for k in ("w1", "w3", "w2")}
+        q_sh = None if t["shared"] is None else tuple(moe.quantize_fp8(a) for a in t["shared"])
+        torch.cuda.synchronize()
+        for k in ("w1", "w3", "w2"):
+            t[k] = None
+        t["shared"] = None
+        torch.cuda.empty_cache()
+        log("expert weights quantised to FP8 E4M3 (per-row scales)")
+
+    def step(debug=None):
+        if fp8:
+            moe.layer_forward_fp8(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"], q["w2"], q_sh,
+                                  y=y, ws=ws, debug=debug)
+        else:
+            moe.layer_forward(d, t["x"], t["wg"], t["bias"], t["w1"], t["w3"], t["w2"],
+                              t["shared"], y=y, ws=ws, debug=debug)
+
+    if fp8:
+        step()
+        torch.cuda.synchronize()
+        quant_err = float(torch.linalg.vector_norm(y.float() - y_ref) / torch.linalg.vector_norm(y_ref))
+        del y_ref
 
     # routing statistics (one extra untimed run)
     counts = torch.empty(w.E, dtype=torch.int32, device=dev)
@@ -131,15 +162,19 @@ def main():
     load["ms"] = round(e0.elapsed_ms(e1) / n_ls, 4)
 
     es = 2 if w.dtype == "bf16" else 4
+    wes = 1 if fp8 else es                      # bytes of one expert weight element
+    sc = lambda rows: 4.0 * rows if fp8 else 0.0  # per-row scales of FP8 weights
     Is = w.I_shared
     F = 2.0 * w.T * w.H * w.E + 6.0 * R * w.H * w.I + 6.0 * w.T * w.H * Is
-    B = (3.0 * w.H * w.I * es * touched + 3.0 * w.H * Is * es + w.E * w.H * es
+    B = (3.0 * w.H * w.I * wes * touched + sc((2 * w.I + w.H) * touched)
+         + 3.0 * w.H * Is * wes + sc(2 * Is + w.H if Is else 0) + w.E * w.H * es
          + 2.0 * w.T * w.H * es)
     gu_avg = float(np.mean(gu_ms))
     # the gate-up kernel's bound: whichever of its algorithmic flops at the MFMA peak and its
     # algorithmic bytes (W1 and W3 of every touched expert and the shared expert, read once, and
     # x) at the HBM peak takes longer
-    gu_bytes = 2.0 * w.H * w.I * es * touched + 2.0 * w.H * Is * es + w.T * w.H * es
+    gu_bytes = (2.0 * w.H * w.I * wes * touched + sc(2 * w.I * touched) + 2.0 * w.H * Is * wes
+                + sc(2 * Is) + w.T * w.H * es)
     gu_flops = 4.0 * R * w.H * w.I + 4.0 * w.T * w.H * Is
     if gu_bytes / (PEAK_HBM_GBS * 1e9) > gu_flops / (PEAK_BF16_TFLOPS * 1e12):
         achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
@@ -149,15 +184,17 @@ def main():
         achieved = gu_flops / (gu_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["traffic"] = profiled_traffic(w.name)
+    roof["traffic"] = profiled_traffic(w.name + ("_fp8" if fp8 else ""))
     # the library takes 256-row tiles when a group holds >= 128 rows on average
     # (the timed span is the grouped GEMM plus the reduction of its split last round of tiles)
     if (w.T * w.k) // w.E >= 128:
-        roof["kernel"] = ("gemm_kernel<TileShape<256,256,2,4,2>, SwiGLU> + gemm_tail_kernel "
-                          "(grouped gate-up, 256x256 tiles)")
+        shape = "TileShape<256,256,2,4,2>"
+        rows = "256x256 tiles"
     else:
-        roof["kernel"] = ("gemm_kernel<TileShape<32,256,1,4,4>, SwiGLU> + gemm_tail_kernel "
-                          "(grouped gate-up, 32-row tiles)")
+        shape = "TileShape<32,256,1,4,3>" if fp8 else "TileShape<32,256,1,4,4>"
+        rows = "32-row tiles"
+    roof["kernel"] = (f"gemm_kernel<{shape}, SwiGLU{', FP8 weights' if fp8 else ''}> + "
+                      f"gemm_tail_kernel (grouped gate-up, {rows})")
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
     layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
@@ -177,14 +214,16 @@ def main():
         "data": "synthetic (seeded normal draws, shapes of the named workload)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "I_shared": Is, "capacity": cap, "accumulate": "fp32",
-                   **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {})},
+                   **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {}),
+                   **({"expert_weights": "fp8_e4m3_per_row_scale"} if fp8 else {})},
         "roofline": roof,
         "layer": {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
                   "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
                   "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
                   "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
                   "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
-                  "load_stats": load},
+                  "load_stats": load,
+                  **({"fp8_vs_bf16_weights_rel_l2": round(quant_err, 5)} if fp8 else {})},
     }
 
     if not args.no_cpu_baseline:

@@ -219,6 +219,46 @@ moe_status_t moe_load_stats(const moe_dims_t* dims, const int32_t* topk_ids, int
                             moe_load_stats_t* stats, float* bias_next, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* FP8 E4M3 weight quantisation, one fp32 scale per row.  [P3] §5.2 serves the
+ * experts with low-precision weights (its configuration: 4-bit weights, FP8
+ * activations) to cut the bytes a decode step streams; the format here is a
+ * reading: E4M3 (OCP: sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * largest finite 448, no infinities) with a per-row scale, activations bf16.
+ *  w [rows, K] of storage `dtype` (MOE_BF16 or MOE_F32), K % 8 == 0, K > 0.
+ *  scales[r] = fp32(max_k |w[r,k]| / 448); q[r,k] = the E4M3 code nearest to
+ *  fp32(w[r,k] / scales[r]) (ties to even, saturating at +-448), 0 when the
+ *  scale is 0.  The dequantised weight is value(q) * scale.
+ *  q [rows, K] u8 and scales [rows] fp32 are device outputs.  For a layer,
+ *  quantise w1 and w3 as [E*I, H], w2 as [E*H, I] (and the shared expert's
+ *  likewise): one scale per output channel. */
+moe_status_t moe_quantize_fp8(int64_t rows, int32_t K, int32_t dtype, const void* w, uint8_t* q,
+                              float* scales, void* stream);
+
+/* moe_expert_ffn with FP8 weights: w1q/w3q [E,I,H], w2q [E,H,I] E4M3 codes
+ * and their per-row scales w1s/w3s [E*I], w2s [E*H] (as moe_quantize_fp8
+ * writes them).  dims->dtype must be MOE_BF16 (x_packed, y_packed bf16).
+ *  y_packed[r] = W2' ( silu(W1' x_packed[r]) * (W3' x_packed[r]) ) with
+ *  W' = value(q) * scale per row: the codes widen exactly to bf16 for the MFMA
+ *  and each output column's fp32 sum is multiplied by its row's scale. */
+moe_status_t moe_expert_ffn_fp8(const moe_dims_t* dims, const void* x_packed,
+                                const int32_t* offsets, const uint8_t* w1q, const float* w1s,
+                                const uint8_t* w3q, const float* w3s, const uint8_t* w2q,
+                                const float* w2s, void* y_packed, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* moe_layer_forward with FP8 expert weights (the gate stays bf16): as
+ * moe_layer_forward, with each expert weight given as E4M3 codes and per-row
+ * scales (moe_quantize_fp8); the shared expert's too when dims->I_shared > 0
+ * (ws1q/ws3q [I_shared,H] with ws1s/ws3s [I_shared], ws2q [H,I_shared] with
+ * ws2s [H]).  dims->dtype must be MOE_BF16. */
+moe_status_t moe_layer_forward_fp8(const moe_dims_t* dims, const void* x, const void* wg,
+                                   const float* bias, const uint8_t* w1q, const float* w1s,
+                                   const uint8_t* w3q, const float* w3s, const uint8_t* w2q,
+                                   const float* w2s, const uint8_t* ws1q, const float* ws1s,
+                                   const uint8_t* ws3q, const float* ws3s, const uint8_t* ws2q,
+                                   const float* ws2s, void* y, const moe_debug_out_t* dbg,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 /* The whole layer in one enqueue: gate, route (+bias, capacity), permute,
  * grouped gate-up with SiLU*mul, grouped down, combine.  The pack is fused into
  * the gate-up GEMM's row loads.  The shared expert (dims->I_shared > 0) runs

@@ -156,6 +156,72 @@ def load_stats(d: Dims, ids, stats, raw_counts=None, bias_next=None, ws=None, st
         "moe_load_stats")
 
 
+def quantize_fp8(w, q=None, scales=None, stream=None):
+    """Per-row FP8 E4M3 quantisation of a bf16 or fp32 device tensor (rows = all leading
+    dimensions).  Returns (codes uint8 of w's shape, scales float32 of w's leading shape)."""
+    dt = {torch.bfloat16: _lib.MOE_BF16, torch.float32: _lib.MOE_F32}.get(w.dtype)
+    if dt is None:
+        raise TypeError(f"quantize_fp8: bf16 or fp32 weights, got {w.dtype}")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _check(_lib.lib().moe_quantize_fp8(rows, K, dt, _ptr(w, None, "w"), _ptr(q, torch.uint8, "q"),
+                                       _ptr(scales, torch.float32, "scales"), _stream(stream)),
+           "moe_quantize_fp8")
+    return q, scales
+
+
+def expert_ffn_fp8(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None):
+    """moe_expert_ffn_fp8; w1, w3, w2 are (codes, scales) pairs from quantize_fp8."""
+    c = d.c()
+    dt = d.torch_dtype
+    (q1, s1), (q3, s3), (q2, s2) = w1, w3, w2
+    u8, f32 = torch.uint8, torch.float32
+    _check(_lib.lib().moe_expert_ffn_fp8(
+        C.byref(c), _ptr(x_packed, dt, "x_packed"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(q1, u8, "w1q"), _ptr(s1, f32, "w1s"), _ptr(q3, u8, "w3q"), _ptr(s3, f32, "w3s"),
+        _ptr(q2, u8, "w2q"), _ptr(s2, f32, "w2s"), _ptr(y_packed, dt, "y_packed"),
+        _ptr(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)),
+        "moe_expert_ffn_fp8")
+
+
+def _debug_struct(debug):
+    types = dict(logits=torch.float32, topk_ids=torch.int32, topk_w=torch.float32,
+                 counts=torch.int32, offsets=torch.int32, pos=torch.int32, n_dropped=torch.int32)
+    dbg = MoeDebugOut(**{k: _ptr(v, types[k], k) for k, v in debug.items() if k != "events"})
+    for i, ev in enumerate(debug.get("events") or []):
+        dbg.events[i] = ev  # raw hipEvent_t handles (or None)
+    return dbg
+
+
+def layer_forward_fp8(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None,
+                      debug=None, stream=None):
+    """The fused layer with FP8 expert weights: w1, w3, w2 (and the three shared-expert weights
+    in `shared`) are (codes, scales) pairs from quantize_fp8.  Returns y."""
+    dt = d.torch_dtype
+    if y is None:
+        y = torch.empty((d.T, d.H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(d, x.device)
+    u8, f32 = torch.uint8, torch.float32
+    none = (None, None)
+    (q1, s1), (q3, s3), (q2, s2) = w1, w3, w2
+    (e1, t1), (e3, t3), (e2, t2) = shared if shared is not None else (none, none, none)
+    dbg = _debug_struct(debug) if debug else None
+    c = d.c()
+    _check(_lib.lib().moe_layer_forward_fp8(
+        C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, f32, "bias"),
+        _ptr(q1, u8, "w1q"), _ptr(s1, f32, "w1s"), _ptr(q3, u8, "w3q"), _ptr(s3, f32, "w3s"),
+        _ptr(q2, u8, "w2q"), _ptr(s2, f32, "w2s"), _ptr(e1, u8, "ws1q"), _ptr(t1, f32, "ws1s"),
+        _ptr(e3, u8, "ws3q"), _ptr(t3, f32, "ws3s"), _ptr(e2, u8, "ws2q"), _ptr(t2, f32, "ws2s"),
+        _ptr(y, dt, "y"), C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"),
+        ws.numel(), _stream(stream)), "moe_layer_forward_fp8")
+    return y
+
+
 def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None, debug=None,
                   stream=None):
     """The fused layer.  shared = (ws1, ws3, ws2) or None; debug: dict of tensors to fill
@@ -168,14 +234,7 @@ def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None
     s1 = s3 = s2 = None
     if shared is not None:
         s1, s3, s2 = shared
-    dbg = None
-    if debug:
-        types = dict(logits=torch.float32, topk_ids=torch.int32, topk_w=torch.float32,
-                     counts=torch.int32, offsets=torch.int32, pos=torch.int32,
-                     n_dropped=torch.int32)
-        dbg = MoeDebugOut(**{k: _ptr(v, types[k], k) for k, v in debug.items() if k != "events"})
-        for i, ev in enumerate(debug.get("events") or []):
-            dbg.events[i] = ev  # raw hipEvent_t handles (or None)
+    dbg = _debug_struct(debug) if debug else None
     c = d.c()
     _check(_lib.lib().moe_layer_forward(
         C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),

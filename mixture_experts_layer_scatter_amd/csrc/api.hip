@@ -179,17 +179,26 @@ PermuteArgs permute_args(const moe_dims_t* d, const Layout& L, void* ws) {
   return a;
 }
 
-// grouped gate-up + down over G groups whose packed row ranges are offsets[0..G]
+// weights of expert FFNs: the layer's storage type (no scales), or FP8 E4M3 codes with one
+// fp32 scale per row (bf16 layers only)
+struct ExpertWeights {
+  const void *w1, *w3, *w2;
+  const float *s1, *s3, *s2;
+  bool fp8() const { return s1 != nullptr; }
+  bool complete() const { return w1 && w3 && w2 && (!s1 || (s3 && s2)) && (s1 || (!s3 && !s2)); }
+};
+
+// grouped gate-up + down over G groups whose packed row ranges are offsets[0..G]; groups past
+// G_routed (at most one) take the extra weights X
 hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row_map,
                    int64_t a_rows, int64_t max_rows, const int32_t* offsets, int G, int G_routed,
-                   const void* w1, const void* w3, const void* w2, const void* e1,
-                   const void* e3, const void* e2, void* act, void* out, int32_t* ts_gu,
-                   int32_t* ts_dn, int avg_rows, float* tail, hipStream_t s,
+                   const ExpertWeights& W, const ExpertWeights* X, void* act, void* out,
+                   int32_t* ts_gu, int32_t* ts_dn, int avg_rows, float* tail, hipStream_t s,
                    void* const* ev = nullptr) {
   const bool bf16 = d->dtype == MOE_BF16;
-  // groups past G_routed take the extra weights; there must be some for them
-  if (G_routed < 0 || G_routed > G || (G > G_routed && (!e1 || !e3 || !e2)) || !w1 || !w3 || !w2)
-    return hipErrorInvalidValue;
+  // groups past G_routed take the extra weights; there must be some for them, stored like W's
+  if (G_routed < 0 || G_routed > G || !W.complete() || (W.fp8() && !bf16)) return hipErrorInvalidValue;
+  if (G > G_routed && (!X || !X->complete() || X->fp8() != W.fp8())) return hipErrorInvalidValue;
   int bm_gu, nt_gu, bm_dn, nt_dn;
   if (bf16) {
     gemm_bf16_tiling(GEMM_GATE_UP, avg_rows, I, &bm_gu, &nt_gu);
@@ -207,11 +216,17 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   gu.row_map = row_map;
   gu.a_rows = a_rows;
   gu.max_rows = max_rows;
-  gu.b = w1;
-  gu.b2 = w3;
+  gu.b = W.w1;
+  gu.b2 = W.w3;
+  gu.b_scale = W.s1;
+  gu.b2_scale = W.s3;
   gu.b_stride = (int64_t)I * d->H;
-  gu.b_extra = e1;
-  gu.b2_extra = e3;
+  if (G > G_routed) {
+    gu.b_extra = X->w1;
+    gu.b2_extra = X->w3;
+    gu.b_scale_extra = X->s1;
+    gu.b2_scale_extra = X->s3;
+  }
   gu.N = I;
   gu.K = d->H;
   gu.c = act;
@@ -226,9 +241,13 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   dn.a = act;
   dn.a_rows = max_rows;
   dn.max_rows = max_rows;
-  dn.b = w2;
+  dn.b = W.w2;
+  dn.b_scale = W.s2;
   dn.b_stride = (int64_t)d->H * I;
-  dn.b_extra = e2;
+  if (G > G_routed) {
+    dn.b_extra = X->w2;
+    dn.b_scale_extra = X->s2;
+  }
   dn.N = d->H;
   dn.K = I;
   dn.c = out;
@@ -362,21 +381,57 @@ moe_status_t moe_permute(const moe_dims_t* d, const void* x, const int32_t* topk
   return MOE_OK;
 }
 
-moe_status_t moe_expert_ffn(const moe_dims_t* d, const void* x_packed, const int32_t* offsets,
-                            const void* w1, const void* w3, const void* w2, void* y_packed,
-                            void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status_t expert_ffn_impl(const moe_dims_t* d, const void* x_packed, const int32_t* offsets,
+                             const ExpertWeights& W, void* y_packed, void* ws, size_t ws_bytes,
+                             void* stream) {
   moe_status_t st = check_dims(d);
   if (st != MOE_OK) return st;
-  if (!offsets || !w1 || !w3 || !w2) return MOE_ERR_INVALID_ARG;
+  if (!offsets || !W.complete()) return MOE_ERR_INVALID_ARG;
+  if (W.fp8() && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->T > 0 && (!x_packed || !y_packed)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(d);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
   const int64_t n = (int64_t)d->T * d->k;
   const int avg = (int)(n / d->E);
-  MOE_TRY(run_ffn(d, d->I, x_packed, nullptr, n, n, offsets, d->E, d->E, w1, w3, w2, nullptr,
-                  nullptr, nullptr, at<void>(ws, L.act), y_packed, at<int32_t>(ws, L.ts_gu),
+  MOE_TRY(run_ffn(d, d->I, x_packed, nullptr, n, n, offsets, d->E, d->E, W, nullptr,
+                  at<void>(ws, L.act), y_packed, at<int32_t>(ws, L.ts_gu),
                   at<int32_t>(ws, L.ts_dn), avg, at<float>(ws, L.tail), (hipStream_t)stream));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_expert_ffn(const moe_dims_t* d, const void* x_packed, const int32_t* offsets,
+                            const void* w1, const void* w3, const void* w2, void* y_packed,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return expert_ffn_impl(d, x_packed, offsets, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr},
+                         y_packed, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_expert_ffn_fp8(const moe_dims_t* d, const void* x_packed,
+                                const int32_t* offsets, const uint8_t* w1q, const float* w1s,
+                                const uint8_t* w3q, const float* w3s, const uint8_t* w2q,
+                                const float* w2s, void* y_packed, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!w1s || !w3s || !w2s) return MOE_ERR_INVALID_ARG;
+  return expert_ffn_impl(d, x_packed, offsets, ExpertWeights{w1q, w3q, w2q, w1s, w3s, w2s},
+                         y_packed, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_quantize_fp8(int64_t rows, int32_t K, int32_t dtype, const void* w, uint8_t* q,
+                              float* scales, void* stream) {
+  if (rows < 0 || K <= 0 || (dtype != MOE_BF16 && dtype != MOE_F32)) return MOE_ERR_INVALID_ARG;
+  if (K % 8) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_quantize_fp8(w, dtype == MOE_BF16, rows, K, q, scales, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -391,17 +446,21 @@ moe_status_t moe_combine(const moe_dims_t* d, const void* y_packed, const int32_
   return MOE_OK;
 }
 
-moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* wg,
-                               const float* bias, const void* w1, const void* w3, const void* w2,
-                               const void* ws1, const void* ws3, const void* ws2, void* y,
-                               const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* wg,
+                                const float* bias, const ExpertWeights& W,
+                                const ExpertWeights& SW, void* y, const moe_debug_out_t* dbg,
+                                void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_dims(d);
   if (st != MOE_OK) return st;
-  if (!x || !wg || !w1 || !w3 || !w2 || !y) {
+  if (!x || !wg || !W.complete() || !y) {
     if (d->T > 0) return MOE_ERR_INVALID_ARG;
   }
-  if (d->I_shared > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_INVALID_ARG;
+  if (W.fp8() && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->I_shared > 0 && (!SW.complete() || SW.fp8() != W.fp8())) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(d);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
@@ -409,7 +468,6 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
   const int T = d->T, E = d->E, k = d->k, n = T * k;
   const bool shared = d->I_shared > 0;
   const bool fold = shared && d->I_shared == d->I;
-
   float* logits = dbg && dbg->logits ? dbg->logits : at<float>(ws, L.logits);
   int32_t* ids = at<int32_t>(ws, L.ids);
   float* w = at<float>(ws, L.w);
@@ -438,8 +496,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
   const int64_t max_rows = (int64_t)n + (fold ? T : 0);
   const int avg = n / E;
   void* yp = at<void>(ws, L.yp);
-  MOE_TRY(run_ffn(d, d->I, x, row_token, T, max_rows, offsets, G, E, w1, w3, w2,
-                  fold ? ws1 : nullptr, fold ? ws3 : nullptr, fold ? ws2 : nullptr,
+  MOE_TRY(run_ffn(d, d->I, x, row_token, T, max_rows, offsets, G, E, W, fold ? &SW : nullptr,
                   at<void>(ws, L.act), yp, at<int32_t>(ws, L.ts_gu), at<int32_t>(ws, L.ts_dn), avg,
                   at<float>(ws, L.tail), s, ev));
   const void* ys = nullptr;
@@ -454,8 +511,8 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
     int32_t* off2 = at<int32_t>(ws, L.raw);  // two ints: [0, T]
     whole_range_kernel<<<1, 1, 0, s>>>(off2, T);
     MOE_TRY(hipGetLastError());
-    MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 1, ws1, ws3, ws2, nullptr, nullptr,
-                    nullptr, at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
+    MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 1, SW, nullptr,
+                    at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
                     at<int32_t>(ws, L.ts_dn), T, at<float>(ws, L.tail), s));
     ys = at<void>(ws, L.yps);
   }
@@ -480,6 +537,34 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
                              hipMemcpyDeviceToDevice, s));
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* wg,
+                               const float* bias, const void* w1, const void* w3, const void* w2,
+                               const void* ws1, const void* ws3, const void* ws2, void* y,
+                               const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return layer_forward_impl(d, x, wg, bias, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr},
+                            ExpertWeights{ws1, ws3, ws2, nullptr, nullptr, nullptr}, y, dbg, ws,
+                            ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_fp8(const moe_dims_t* d, const void* x, const void* wg,
+                                   const float* bias, const uint8_t* w1q, const float* w1s,
+                                   const uint8_t* w3q, const float* w3s, const uint8_t* w2q,
+                                   const float* w2s, const uint8_t* ws1q, const float* ws1s,
+                                   const uint8_t* ws3q, const float* ws3s, const uint8_t* ws2q,
+                                   const float* ws2s, void* y, const moe_debug_out_t* dbg,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (d && d->T > 0 && (!w1s || !w3s || !w2s)) return MOE_ERR_INVALID_ARG;
+  if (d && d->I_shared > 0 && (!ws1s || !ws3s || !ws2s)) return MOE_ERR_INVALID_ARG;
+  return layer_forward_impl(d, x, wg, bias, ExpertWeights{w1q, w3q, w2q, w1s, w3s, w2s},
+                            ExpertWeights{ws1q, ws3q, ws2q, ws1s, ws3s, ws2s}, y, dbg, ws,
+                            ws_bytes, stream);
 }
 
 }  // extern "C"

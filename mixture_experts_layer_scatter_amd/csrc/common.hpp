@@ -91,6 +91,13 @@ struct GroupedGemm {
   int64_t b_stride;          // elements between consecutive groups' matrices
   const void* b_extra;       // the always-on group (index G_routed), or null
   const void* b2_extra;
+  // FP8 E4M3 weights (one byte per element; bf16 MFMA path only): per-row fp32 scales, group g
+  // of b at b_scale + g * N, of b2 at b2_scale + g * N, the extra group's at *_scale_extra.
+  // Null b_scale: b and b2 hold the layer's storage type.
+  const float* b_scale;
+  const float* b2_scale;
+  const float* b_scale_extra;
+  const float* b2_scale_extra;
   int N, K;                  // output columns, reduction length
   // output C [*, ldc]
   void* c;
@@ -118,6 +125,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& g, int max_rows_pe
                             int num_cus, hipStream_t s);
 // bytes of GroupedGemm::tail_part needed by launch_gemm_bf16 for this kind and group size
 size_t gemm_tail_bytes(int avg_rows_per_group);
+
+// quant.hip: per-row FP8 E4M3 quantisation of a [rows, K] bf16 or fp32 matrix (K % 8 == 0)
+hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
+                               float* scales, hipStream_t s);
 
 // out[i] = sum_s part[s * n + i] (fixed order)
 hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out, hipStream_t s);

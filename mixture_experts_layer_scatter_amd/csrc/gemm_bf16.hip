@@ -48,6 +48,11 @@
 //    applies silu(a) * g before one bf16 store of the activation.
 //  * The gate (fp32 logits) can split its reduction over ksplit workgroups per
 //    tile; the partial sums are added in a fixed order afterwards.
+//  * FP8 weights (WQ): the weight tile travels HBM -> LDS as E4M3 bytes (half
+//    the bytes of bf16, the point for the weight-streaming decode shape); a
+//    fragment read takes 8 codes and widens them to bf16 in registers (every
+//    E4M3 value is exact in bf16), so the same bf16 MFMA runs; the per-row scale
+//    multiplies the fp32 accumulator in the epilogue (it factors out of the sum).
 #include "common.hpp"
 
 namespace moe {
@@ -103,6 +108,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // swizzle of the 16-byte chunks of a 128-byte LDS row: distinct banks for the 8 (and the 16)
 // consecutive rows that one fragment read serves per cycle
 __device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// the same for the 64-byte rows of an FP8 weight tile (four 16-byte chunks); it depends on
+// bits 1..4 of the row only, so a fragment's rows (32 apart) share it
+__device__ __forceinline__ int row_swizzle4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// eight E4M3 codes -> eight bf16 values (exact: the upper half of each fp32 conversion)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 v) {
+  union {
+    uint32_t u[4];
+    bf16x8 h;
+  } r;
+  const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);  // codes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);   // codes 2, 3
+    r.u[2 * i] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+    r.u[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+  }
+  return r.h;
+}
 
 template <int BM_, int BN_, int WM_, int WN_, int S_>
 struct TileShape {
@@ -111,19 +136,35 @@ struct TileShape {
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wavefront tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32 x 32 MFMA blocks per wavefront
   static constexpr int KK = kBK / 16;                 // MFMA k-steps per LDS stage
-  static constexpr int RPL = 1024 / kRowBytes;        // rows one 1 KB wavefront load covers
-  static constexpr int A_LOADS = BM / RPL / WAVES, B_LOADS = BN / RPL / WAVES;
-  static constexpr int L = A_LOADS + B_LOADS;         // loads per wavefront per stage
-  static constexpr int A_BYTES = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
-  static constexpr int LDS = S * STAGE;
+  static constexpr int RPL = 1024 / kRowBytes;        // A rows one 1 KB wavefront load covers
+  static constexpr int A_LOADS = BM / RPL / WAVES;
+  static constexpr int A_BYTES = BM * kRowBytes;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wavefront tile is a multiple of 32 x 32");
-  static_assert(A_LOADS * RPL * WAVES == BM && B_LOADS * RPL * WAVES == BN, "load split");
-  static_assert(S >= 2 && (S - 2) * L < 64, "stages in flight fit the vmcnt counter");
+  static_assert(A_LOADS * RPL * WAVES == BM, "load split");
+};
+
+// LDS geometry of a shape with bf16 (WQ = false) or E4M3 (WQ = true) weights
+template <class SH, bool WQ>
+struct Geo {
+  static constexpr int B_ROWB = WQ ? kBK : kRowBytes;  // bytes of one weight row of a k-step
+  static constexpr int B_RPL = 1024 / B_ROWB;         // weight rows one 1 KB load covers
+  static constexpr int B_LOADS = SH::BN / B_RPL / SH::WAVES;
+  static constexpr int L = SH::A_LOADS + B_LOADS;     // loads per wavefront per stage
+  static constexpr int STAGE = SH::A_BYTES + SH::BN * B_ROWB;
+  static constexpr int LDS = SH::S * STAGE;
+  static_assert(B_LOADS * B_RPL * SH::WAVES == SH::BN, "load split");
+  static_assert(SH::S >= 2 && (SH::S - 2) * L < 64, "stages in flight fit the vmcnt counter");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 using PrefillShape = TileShape<256, 256, 2, 4, 2>;
 using DecodeShape = TileShape<32, 256, 1, 4, 4>;
+// FP8 weights halve the weight tile.  Decode: three 20 KB stages leave room for two workgroups
+// per CU (eight wavefronts with their loads in flight), which streams the weights faster than
+// one workgroup with seven stages (measured: 1.50 against 2.09 ms for the DeepSeek-shaped
+// gate-up).  Prefill: two stages, as for bf16 (a third stage measured slower).
+using PrefillShapeFp8 = TileShape<256, 256, 2, 4, 2>;
+using DecodeShapeFp8 = TileShape<32, 256, 1, 4, 3>;
 
 // ---- tile bookkeeping shared by the GEMM and its tail reduction ---------------------------------
 
@@ -182,13 +223,42 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int xcd, int nx, int kt
 }
 
 // The epilogue: lane holds token l32 of block i and columns 8q + 4hi + (0..3) of each
-// 32-column block j (the weights were the MFMA's first operand: D[column][token]).
-template <class SH, int EPI>
+// 32-column block j (the weights were the MFMA's first operand: D[column][token]).  With FP8
+// weights each column's accumulator is first multiplied by its weight row's scale.
+template <class SH, int EPI, bool WQ>
 __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& t, int ks,
                                            const f32x16 (&acc)[SH::TM][SH::TN], int wm, int wn,
                                            int l32, int hi, int i_only = -1) {
   constexpr int BN = SH::BN, TM = SH::TM, TN = SH::TN;
   const int64_t out_row0 = (int64_t)t.row_base + t.m0;
+  // per-column scales of this tile (1 for bf16 weights), loaded once for all token blocks
+  float4 sc[TN][4];
+  if constexpr (WQ) {
+    const bool extra = p.tile_start && t.g >= p.G_routed;
+    const float* s1 = extra ? p.b_scale_extra : p.b_scale + (int64_t)t.g * p.N;
+    const float* s2 = EPI != EPI_SWIGLU ? s1
+                      : extra ? p.b2_scale_extra : p.b2_scale + (int64_t)t.g * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // SwiGLU: blocks j (W1) and j + 1 (W3) hold the same 32 columns
+        const int col = EPI == EPI_SWIGLU
+                            ? t.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32 + 8 * q + 4 * hi
+                            : t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
+        const float* src = (EPI == EPI_SWIGLU && (j & 1)) ? s2 : s1;
+        sc[j][q] = col < p.N ? *(const float4*)(src + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  }
+  auto scaled = [&](int i, int j, int q, int e) -> float {
+    if constexpr (WQ) {
+      const float4 v = sc[j][q];
+      const float f = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+      return acc[i][j][4 * q + e] * f;
+    } else {
+      return acc[i][j][4 * q + e];
+    }
+  };
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i_only >= 0 && i != i_only) continue;
@@ -205,7 +275,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
           if (col < p.N) {
             float h[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = silu_fast(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
+            for (int e = 0; e < 4; ++e) h[e] = silu_fast(scaled(i, j, q, e)) * scaled(i, j + 1, q, e);
             uint2 v;
             v.x = pack_bf16x2(h[0], h[1]);
             v.y = pack_bf16x2(h[2], h[3]);
@@ -221,8 +291,8 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
           const int col = t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
           if (col < p.N) {
             uint2 v;
-            v.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-            v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            v.x = pack_bf16x2(scaled(i, j, q, 0), scaled(i, j, q, 1));
+            v.y = pack_bf16x2(scaled(i, j, q, 2), scaled(i, j, q, 3));
             *(uint2*)(crow + col) = v;
           }
         }
@@ -234,12 +304,12 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
         for (int q = 0; q < 4; ++q) {
           const int col = t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
           if (col + 3 < p.N && (p.ldc & 3) == 0) {
-            *(float4*)(crow + col) = make_float4(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
-                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *(float4*)(crow + col) = make_float4(scaled(i, j, q, 0), scaled(i, j, q, 1),
+                                                 scaled(i, j, q, 2), scaled(i, j, q, 3));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (col + e < p.N) crow[col + e] = acc[i][j][4 * q + e];
+              if (col + e < p.N) crow[col + e] = scaled(i, j, q, e);
           }
         }
     }
@@ -254,10 +324,13 @@ __device__ __forceinline__ float4* tail_slot(const GroupedGemm& p, int xcd, int 
   return (float4*)(p.tail_part + ((int64_t)xcd * kTailPieces + slot) * kRegs * SH::THREADS);
 }
 
-template <class SH, int EPI, bool GATHER, int GN>
+template <class SH, int EPI, bool GATHER, int GN, bool WQ>
 __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
-  constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, L = SH::L;
+  using GE = Geo<SH, WQ>;
+  constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, L = GE::L;
   constexpr int TM = SH::TM, TN = SH::TN, KK = SH::KK, RPL = SH::RPL;
+  constexpr int B_ROWB = GE::B_ROWB, B_RPL = GE::B_RPL, B_LOADS = GE::B_LOADS;
+  constexpr int STAGE = GE::STAGE, WB = WQ ? 1 : 2;  // weight bytes per element
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs W1 and W3 blocks");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -275,9 +348,9 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * 2));
 
   const int l32 = lane & 31, hi = lane >> 5;
-  const int sw = row_swizzle(l32);
+  const int sw = row_swizzle(l32), sw4 = row_swizzle4(l32);
   const uint32_t a_frag = (uint32_t)((wm * SH::WTM + l32) * kRowBytes);
-  const uint32_t b_frag = (uint32_t)(SH::A_BYTES + (wn * SH::WTN + l32) * kRowBytes);
+  const uint32_t b_frag = (uint32_t)(SH::A_BYTES + (wn * SH::WTN + l32) * B_ROWB);
 
   struct Tile {
     TileLoc loc;
@@ -307,7 +380,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   };
 
   // per-lane source offsets of the current tile's loads (lane: row lane / 8, chunk lane % 8)
-  uint32_t a_off[SH::A_LOADS], b_off[SH::B_LOADS];
+  uint32_t a_off[SH::A_LOADS], b_off[B_LOADS];
   __amdgpu_buffer_rsrc_t rB, rB2;
   int kt0 = 0, ktn = 0;
   auto setup = [&](const Tile& t) {
@@ -317,11 +390,11 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     ktn = __builtin_amdgcn_readfirstlane(t.ktn);
     const bool extra = p.tile_start && t.loc.g >= p.G_routed;
     const char* bbase =
-        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * 2);
+        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * WB);
     const char* b2base = bbase;
     if (EPI == EPI_SWIGLU)
-      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * 2);
-    const uint32_t b_bytes = (uint32_t)((int64_t)p.N * K * 2);
+      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * WB);
+    const uint32_t b_bytes = (uint32_t)((int64_t)p.N * K * WB);
     rB = make_rsrc(bbase, b_bytes);
     rB2 = make_rsrc(b2base, b_bytes);
 #pragma unroll
@@ -337,27 +410,29 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       a_off[i] = off;
     }
 #pragma unroll
-    for (int i = 0; i < SH::B_LOADS; ++i) {
-      const int n = (wid * SH::B_LOADS + i) * RPL + lane / 8;
-      const int c = (lane & 7) ^ row_swizzle(n);
+    for (int i = 0; i < B_LOADS; ++i) {
+      // lane: weight row lane / (chunks per row), chunk lane % (chunks per row)
+      const int n = (wid * B_LOADS + i) * B_RPL + (WQ ? lane / 4 : lane / 8);
+      const int c = WQ ? (lane & 3) ^ row_swizzle4(n) : (lane & 7) ^ row_swizzle(n);
       const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
-      b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * 2u + c * 16 : kOutOfRange;
+      b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * WB + c * 16 : kOutOfRange;
     }
   };
   // local k-step lk of the current tile into LDS slot `slot`; lk >= ktn loads nothing
   auto issue = [&](int lk, int slot) {
     const bool valid = lk < ktn;
-    char* sa = smem + slot * SH::STAGE;
+    char* sa = smem + slot * STAGE;
     char* sb = sa + SH::A_BYTES;
     const int kb = valid ? (kt0 + lk) * kRowBytes : 0;
+    const int kbw = valid ? (kt0 + lk) * B_ROWB : 0;
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i)
       load_lds16(rA, sa + (wid * SH::A_LOADS + i) * 1024, valid ? a_off[i] : kOutOfRange, kb);
 #pragma unroll
-    for (int i = 0; i < SH::B_LOADS; ++i) {
-      const int blk = wid * SH::B_LOADS + i;
-      const bool second = EPI == EPI_SWIGLU && (((blk * RPL) >> 5) & 1);
-      load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kb);
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int blk = wid * B_LOADS + i;
+      const bool second = EPI == EPI_SWIGLU && (((blk * B_RPL) >> 5) & 1);
+      load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kbw);
     }
   };
   auto prologue = [&]() {
@@ -371,8 +446,16 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 32 * kRowBytes);
+    if constexpr (WQ) {
+      // 8 codes = half of the 16-byte chunk kk of the 64-byte row
+      const uint32_t woff = (uint32_t)(((kk ^ sw4) * 16) + hi * 8);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + coff + j * 32 * kRowBytes);
+      for (int j = 0; j < TN; ++j)
+        fb[buf][j] = fp8x8_to_bf16(*(const uint2*)(st + b_frag + woff + j * 32 * B_ROWB));
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + coff + j * 32 * kRowBytes);
+    }
   };
   // weights as the first operand: D[column][token]
   auto mfmas = [&](int buf) {
@@ -388,8 +471,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     read_frags(smem, 0, 0);
     issue(S - 1, S - 1);
     for (int lk = 0; lk < ktn; ++lk) {
-      const char* cur = smem + (lk % S) * SH::STAGE;
-      const char* nxt = smem + ((lk + 1) % S) * SH::STAGE;
+      const char* cur = smem + (lk % S) * STAGE;
+      const char* nxt = smem + ((lk + 1) % S) * STAGE;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         if (kk < KK - 1) {
@@ -454,7 +537,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
             dst[((i * TN + j) * 4 + q) * SH::THREADS] =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     } else {
-      store_tile<SH, EPI>(p, done.loc, done.ks, acc, wm, wn, l32, hi);
+      store_tile<SH, EPI, WQ>(p, done.loc, done.ks, acc, wm, wn, l32, hi);
     }
     if (!more) break;
   }
@@ -462,7 +545,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 
 // The split tail tiles: add each tile's fp32 partials in piece order, then the epilogue.  One
 // workgroup per (XCD, tail tile, token block i), so the reduction spreads over many CUs.
-template <class SH, int EPI, int GN>
+template <class SH, int EPI, int GN, bool WQ>
 __global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, int nx) {
   constexpr int TM = SH::TM, TN = SH::TN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -497,17 +580,18 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, i
     }
   }
   const TileLoc loc = locate_tile<SH, GN>(p, plan.lo + plan.full * nx + t);
-  store_tile<SH, EPI>(p, loc, 0, acc, wm, wn, lane & 31, lane >> 5, ib);
+  store_tile<SH, EPI, WQ>(p, loc, 0, acc, wm, wn, lane & 31, lane >> 5, ib);
 }
 
-template <class SH, int EPI, bool GATHER, int GN>
+template <class SH, int EPI, bool GATHER, int GN, bool WQ = false>
 static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStream_t s) {
-  auto kern = gemm_kernel<SH, EPI, GATHER, GN>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
+  constexpr int LDS = Geo<SH, WQ>::LDS;
+  auto kern = gemm_kernel<SH, EPI, GATHER, GN, WQ>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
   if (e != hipSuccess) return e;
   if (max_tiles <= 0) return hipSuccess;
   // workgroups per CU: as many as the LDS holds, at most 8 wavefronts per CU
-  int per_cu = (160 * 1024) / SH::LDS;
+  int per_cu = (160 * 1024) / LDS;
   const int by_waves = 8 / SH::WAVES;
   if (per_cu > by_waves) per_cu = by_waves;
   if (per_cu < 1) per_cu = 1;
@@ -516,10 +600,10 @@ static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStrea
   grid = (grid + 7) / 8 * 8;
   GroupedGemm q = p;
   if (!q.tile_start || q.ksplit > 1 || EPI == EPI_F32 || grid / 8 > kTailPieces) q.tail_part = nullptr;
-  kern<<<grid, SH::THREADS, SH::LDS, s>>>(q);
+  kern<<<grid, SH::THREADS, LDS, s>>>(q);
   e = hipGetLastError();
   if (e != hipSuccess || !q.tail_part) return e;
-  gemm_tail_kernel<SH, EPI, GN><<<8 * kTailPieces * SH::TM, SH::THREADS, 0, s>>>(q, grid / 8);
+  gemm_tail_kernel<SH, EPI, GN, WQ><<<8 * kTailPieces * SH::TM, SH::THREADS, 0, s>>>(q, grid / 8);
   return hipGetLastError();
 }
 
@@ -566,8 +650,22 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
     return run<TileShape<32, 256, 1, 4, 4>, EPI_F32, false, 1>(p, mt, num_cus, s);
   }
   const bool big = bm == PrefillShape::BM;
+  const bool gather = p.row_map != nullptr;
+  if (p.b_scale) {  // FP8 weights
+    if (kind == GEMM_GATE_UP && !p.b2_scale) return hipErrorInvalidValue;
+    if (p.G > p.G_routed && (!p.b_scale_extra || (kind == GEMM_GATE_UP && !p.b2_scale_extra)))
+      return hipErrorInvalidValue;
+    if (kind == GEMM_GATE_UP) {
+      if (big)
+        return gather ? run<PrefillShapeFp8, EPI_SWIGLU, true, 8, true>(p, mt, num_cus, s)
+                      : run<PrefillShapeFp8, EPI_SWIGLU, false, 8, true>(p, mt, num_cus, s);
+      return gather ? run<DecodeShapeFp8, EPI_SWIGLU, true, 1, true>(p, mt, num_cus, s)
+                    : run<DecodeShapeFp8, EPI_SWIGLU, false, 1, true>(p, mt, num_cus, s);
+    }
+    if (big) return run<PrefillShapeFp8, EPI_BF16, false, 8, true>(p, mt, num_cus, s);
+    return run<DecodeShapeFp8, EPI_BF16, false, 1, true>(p, mt, num_cus, s);
+  }
   if (kind == GEMM_GATE_UP) {
-    const bool gather = p.row_map != nullptr;
     if (big)
       return gather ? run<PrefillShape, EPI_SWIGLU, true, 8>(p, mt, num_cus, s)
                     : run<PrefillShape, EPI_SWIGLU, false, 8>(p, mt, num_cus, s);

@@ -21,7 +21,7 @@ def _lib():
 def test_exports_every_declared_symbol():
     L = _lib()
     header = open(os.path.join(ROOT, "include", "moe.h")).read()
-    declared = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", header))
     assert declared == set(L.EXPORTS), declared ^ set(L.EXPORTS)
     raw = C.CDLL(L.LIB_PATH)
     for name in declared:
@@ -150,3 +150,33 @@ def test_load_stats_argument_checks():
     assert lib.moe_load_stats(C.byref(d0), p, None, p, p, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_load_stats(C.byref(d), p, None, p, None, None, 0, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_load_stats(C.byref(d), p, None, p, None, p, 16, None) == L.MOE_ERR_WORKSPACE
+
+
+def test_fp8_entry_point_checks():
+    L = _lib()
+    lib = L.lib()
+    p = C.c_void_p(16)  # never dereferenced
+    # quantisation: bad K, dtype, rows; K % 8 unsupported; rows == 0 is a no-op
+    assert lib.moe_quantize_fp8(4, 0, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(4, 64, 7, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(-1, 64, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(4, 60, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_fp8(4, 64, L.MOE_BF16, None, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(0, 64, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    # FP8 FFN and layer: scales required, bf16 layers only
+    d = _dims()
+    assert lib.moe_expert_ffn_fp8(C.byref(d), p, p, p, None, p, p, p, p, p, p, 1 << 40,
+                                  None) == L.MOE_ERR_INVALID_ARG
+    d32 = _dims(dtype=L.MOE_F32)
+    assert lib.moe_expert_ffn_fp8(C.byref(d32), p, p, p, p, p, p, p, p, p, p, 1 << 40,
+                                  None) == L.MOE_ERR_UNSUPPORTED
+    # x, wg, bias, w1q, w1s, w3q, w3s, w2q, w2s, ws1q, ws1s, ws3q, ws3s, ws2q, ws2s, y
+    args = [p] * 16
+    args[4] = None  # w1 scales missing
+    assert lib.moe_layer_forward_fp8(C.byref(d), *args, None, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward_fp8(C.byref(d32), *([p] * 16), None, p, 1 << 40,
+                                     None) == L.MOE_ERR_UNSUPPORTED
+    ds = _dims(I_shared=64)
+    args = [p] * 16
+    args[10] = None  # shared-expert W1 scales missing
+    assert lib.moe_layer_forward_fp8(C.byref(ds), *args, None, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
