@@ -38,6 +38,9 @@ def main():
     ap.add_argument("--weights", choices=("same", "fp8"), default="same",
                     help="expert weights in the layer's storage type, or FP8 E4M3 with per-row "
                          "scales (quantised once before timing; bf16 layers)")
+    ap.add_argument("--cache-slots", type=int, default=0,
+                    help="also measure the layer with its routed experts in an HBM expert cache "
+                         "of this many slots, filled from pinned host memory (cold and warm)")
     ap.add_argument("--bias-mode", choices=("softmax", "select"), default="softmax",
                     help="how a workload's routing bias enters: inside the softmax, or ranking only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,6 +164,10 @@ def main():
     load = {f: (round(v, 4) if isinstance(v, float) else v) for f, v in moe.read_load_stats(st).items()}
     load["ms"] = round(e0.elapsed_ms(e1) / n_ls, 4)
 
+    cache_res = None
+    if args.cache_slots > 0 and not fp8:
+        cache_res = measure_cache(moe, d, t, args.cache_slots, ms_per_step, log)
+
     es = 2 if w.dtype == "bf16" else 4
     wes = 1 if fp8 else es                      # bytes of one expert weight element
     sc = lambda rows: 4.0 * rows if fp8 else 0.0  # per-row scales of FP8 weights
@@ -223,7 +230,8 @@ def main():
                   "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
                   "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
                   "load_stats": load,
-                  **({"fp8_vs_bf16_weights_rel_l2": round(quant_err, 5)} if fp8 else {})},
+                  **({"fp8_vs_bf16_weights_rel_l2": round(quant_err, 5)} if fp8 else {}),
+                  **({"expert_cache": cache_res} if cache_res is not None else {})},
     }
 
     if not args.no_cpu_baseline:
@@ -240,6 +248,60 @@ def kernel_source_digest():
         with open(os.path.join(ROOT, "mixture_experts_layer_scatter_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def measure_cache(moe, d, t, slots, uncached_ms, log):
+    """The layer with its routed experts in an HBM expert cache of `slots` slots, filled from
+    pinned host memory: the first (cold) call loads every expert the batch needs over PCIe, the
+    later (warm) calls find them resident.  Also times a plain pinned host-to-device copy of the
+    same bytes on the same copy stream, the PCIe reference."""
+    import numpy as np
+    import torch
+    log(f"expert cache: {slots} slots, pinning host copies of the expert weights")
+    host = []
+    for k in ("w1", "w3", "w2"):
+        h = torch.empty(t[k].shape, dtype=t[k].dtype, pin_memory=True)
+        h.copy_(t[k])
+        host.append(h)
+    cache = moe.ExpertCache(d, slots, *host)
+    copy = torch.cuda.Stream()
+    ws = moe.workspace(d)
+    y = torch.empty((d.T, d.H), dtype=d.torch_dtype, device=t["x"].device)
+
+    def run():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, info = moe.layer_forward_cached(d, t["x"], t["wg"], t["bias"], cache, t["shared"], y=y,
+                                           ws=ws, copy_stream=copy)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3, info
+
+    try:
+        cold_ms, cold = run()
+    except moe.MoeError as e:
+        cache.close()
+        return {"slots": slots, "error": str(e)}
+    warm = [run() for _ in range(10)]
+    warm_ms = float(np.median([m for m, _ in warm]))
+    # PCIe reference: the same bytes as one pinned host-to-device copy per expert
+    nbytes = int(cold["bytes_loaded"])
+    per = nbytes // max(cold["loads"], 1)
+    dst = torch.empty(per, dtype=torch.uint8, device=y.device)
+    src = torch.empty(per, dtype=torch.uint8, pin_memory=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(copy):
+        for _ in range(max(cold["loads"], 1)):
+            dst.copy_(src, non_blocking=True)
+    copy.synchronize()
+    copy_ms = (time.perf_counter() - t0) * 1e3
+    cache.close()
+    load_ms = max(cold_ms - warm_ms, 1e-6)
+    return {"slots": slots, "cold_ms": round(cold_ms, 3), "warm_ms": round(warm_ms, 3),
+            "uncached_ms": round(uncached_ms, 3), "cold_loads": cold["loads"],
+            "warm_hits": warm[-1][1]["hits"], "bytes_loaded": nbytes,
+            "h2d_gbs_in_layer": round(nbytes / load_ms / 1e6, 1),
+            "h2d_gbs_plain_copy": round(nbytes / copy_ms / 1e6, 1)}
 
 
 def profiled_traffic(workload):

@@ -259,6 +259,71 @@ moe_status_t moe_layer_forward_fp8(const moe_dims_t* dims, const void* x, const 
                                    const float* ws2s, void* y, const moe_debug_out_t* dbg,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Expert cache: experts resident in HBM up to a number of slots ----------
+ * [P3] §3.2 keeps a subset of the experts in HBM and loads the others from
+ * host memory before a batch needs them, evicting the least recently used
+ * resident experts.  Here: a caller-allocated device pool of `slots` expert
+ * slots (W1, W3, W2 of one expert each, in the layer's storage type) and a
+ * device table expert -> slot, managed by a host-side object.  Residency
+ * policy (readings): recency = the last batch that requested an expert (ties:
+ * lower id); a batch's own experts are never evicted for it; free slots are
+ * taken lowest first; missing experts load in ascending id order.
+ * Loads are hipMemcpyAsync host -> device on a copy stream (the host weights
+ * should be pinned, e.g. hipHostMalloc, for the copies to be asynchronous).
+ * Ordering: the copies into evicted slots start after the work enqueued so
+ * far on the compute stream (which may still read those slots) and after
+ * every earlier copy of this cache; the compute stream's later work waits for
+ * every copy of this cache enqueued so far.  The copies thus run
+ * asynchronously to the host and to other streams.  bf16 layers only.  The object holds host bookkeeping (allocated in moe_cache_create, freed
+ * in moe_cache_destroy) and two HIP events; one object must not be used from
+ * two threads at once. */
+typedef struct moe_expert_cache moe_expert_cache_t;
+
+/* Outcome of one batch's residency request. */
+typedef struct {
+  int32_t requested;    /* distinct experts the batch needs      */
+  int32_t hits;         /* of those, already resident            */
+  int32_t loads;        /* copied from host memory               */
+  int32_t evictions;    /* resident experts dropped to make room */
+  int64_t bytes_loaded; /* host -> device bytes enqueued         */
+} moe_cache_step_t;
+
+/* Device bytes of a pool of `slots` expert slots plus the expert -> slot table
+ * (0 on invalid dims or slots < 1). */
+size_t moe_cache_pool_bytes(const moe_dims_t* dims, int32_t slots);
+
+/* host_w1/host_w3 [E,I,H], host_w2 [E,H,I] (host memory, dims->dtype, owned by
+ * the caller and kept alive as long as the cache); pool: device memory of at
+ * least moe_cache_pool_bytes.  Only H, E, I and dtype of dims matter here.
+ * On success *cache receives the new object. */
+moe_status_t moe_cache_create(const moe_dims_t* dims, int32_t slots, const void* host_w1,
+                              const void* host_w3, const void* host_w2, void* pool,
+                              size_t pool_bytes, moe_expert_cache_t** cache);
+void moe_cache_destroy(moe_expert_cache_t* cache);
+
+/* Make the n experts in `experts` (host array, ids in [0, E), duplicates
+ * allowed) resident: enqueue their copies on copy_stream, the table update
+ * on stream, and make stream wait for the copies.  More distinct experts than
+ * slots: MOE_ERR_UNSUPPORTED, nothing changes.  info (host) may be NULL. */
+moe_status_t moe_cache_load(moe_expert_cache_t* cache, const int32_t* experts, int32_t n,
+                            void* copy_stream, void* stream, moe_cache_step_t* info);
+
+/* Host copy of the expert -> slot table (-1: not resident), slot_of [E]. */
+moe_status_t moe_cache_slots(const moe_expert_cache_t* cache, int32_t* slot_of);
+
+/* moe_layer_forward with the routed experts' weights in an expert cache: after
+ * the gate, route and permute, the per-expert row counts come back to the host
+ * (this call waits for `stream` there), the experts with rows are made
+ * resident (moe_cache_load on copy_stream), and the grouped GEMMs read each
+ * expert's weights from its slot.  The shared expert (dims->I_shared > 0) is
+ * given as in moe_layer_forward and is not cached.  The output is bit for bit
+ * that of moe_layer_forward with the same weights.  info (host) may be NULL. */
+moe_status_t moe_layer_forward_cached(const moe_dims_t* dims, const void* x, const void* wg,
+                                      const float* bias, moe_expert_cache_t* cache,
+                                      const void* ws1, const void* ws3, const void* ws2, void* y,
+                                      const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                      void* stream, void* copy_stream, moe_cache_step_t* info);
+
 /* The whole layer in one enqueue: gate, route (+bias, capacity), permute,
  * grouped gate-up with SiLU*mul, grouped down, combine.  The pack is fused into
  * the gate-up GEMM's row loads.  The shared expert (dims->I_shared > 0) runs

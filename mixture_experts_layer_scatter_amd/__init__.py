@@ -5,6 +5,7 @@ thin torch binding.  Submodules load the library on first use and raise when it
 has not been built.
 """
 from ._lib import LIB_PATH, MoeError, EXPORTS  # noqa: F401
-from .api import (Dims, capacity, combine, expert_ffn, expert_ffn_fp8, gate,  # noqa: F401
-                  layer_forward, layer_forward_fp8, load_stats, load_stats_buffer, permute,
-                  quantize_fp8, read_load_stats, route, workspace, workspace_bytes)
+from .api import (Dims, ExpertCache, capacity, combine, expert_ffn, expert_ffn_fp8,  # noqa: F401
+                  gate, layer_forward, layer_forward_cached, layer_forward_fp8, load_stats,
+                  load_stats_buffer, permute, quantize_fp8, read_load_stats, route, workspace,
+                  workspace_bytes)

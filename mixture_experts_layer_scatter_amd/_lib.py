@@ -14,7 +14,9 @@ MOE_F32, MOE_BF16 = 0, 1
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_capacity", "moe_workspace_bytes", "moe_gate", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_load_stats", "moe_quantize_fp8",
-           "moe_expert_ffn_fp8", "moe_layer_forward", "moe_layer_forward_fp8")
+           "moe_expert_ffn_fp8", "moe_cache_pool_bytes", "moe_cache_create", "moe_cache_destroy",
+           "moe_cache_load", "moe_cache_slots", "moe_layer_forward", "moe_layer_forward_fp8",
+           "moe_layer_forward_cached")
 MOE_BIAS_SOFTMAX, MOE_BIAS_SELECT = 0, 1
 
 
@@ -29,6 +31,11 @@ class MoeLoadStats(C.Structure):
                 ("hottest", C.c_int32), ("min_count", C.c_int32), ("idle", C.c_int32),
                 ("mean", C.c_float), ("stddev", C.c_float), ("cv", C.c_float),
                 ("max_over_mean", C.c_float), ("drop_rate", C.c_float)]
+
+
+class MoeCacheStep(C.Structure):
+    _fields_ = [("requested", C.c_int32), ("hits", C.c_int32), ("loads", C.c_int32),
+                ("evictions", C.c_int32), ("bytes_loaded", C.c_int64)]
 
 
 class MoeDebugOut(C.Structure):
@@ -83,6 +90,19 @@ def lib():
         L.moe_expert_ffn_fp8.argtypes = [D, p, p, p, p, p, p, p, p, p, p, sz, p]
         L.moe_layer_forward_fp8.restype = i32
         L.moe_layer_forward_fp8.argtypes = [D] + [p] * 16 + [C.POINTER(MoeDebugOut), p, sz, p]
+        L.moe_cache_pool_bytes.restype = sz
+        L.moe_cache_pool_bytes.argtypes = [D, i32]
+        L.moe_cache_create.restype = i32
+        L.moe_cache_create.argtypes = [D, i32, p, p, p, p, sz, C.POINTER(p)]
+        L.moe_cache_destroy.restype = None
+        L.moe_cache_destroy.argtypes = [p]
+        L.moe_cache_load.restype = i32
+        L.moe_cache_load.argtypes = [p, p, i32, p, p, C.POINTER(MoeCacheStep)]
+        L.moe_cache_slots.restype = i32
+        L.moe_cache_slots.argtypes = [p, p]
+        L.moe_layer_forward_cached.restype = i32
+        L.moe_layer_forward_cached.argtypes = [D, p, p, p, p, p, p, p, p, C.POINTER(MoeDebugOut),
+                                               p, sz, p, p, C.POINTER(MoeCacheStep)]
         L.moe_layer_forward.restype = i32
         L.moe_layer_forward.argtypes = [D, p, p, p, p, p, p, p, p, p, p, C.POINTER(MoeDebugOut), p,
                                         sz, p]

@@ -13,7 +13,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeDebugOut, MoeDims, MoeError, MoeLoadStats
+from ._lib import MoeCacheStep, MoeDebugOut, MoeDims, MoeError, MoeLoadStats
 
 _DT = {"bf16": _lib.MOE_BF16, "f32": _lib.MOE_F32}
 _BIAS = {"softmax": _lib.MOE_BIAS_SOFTMAX, "select": _lib.MOE_BIAS_SELECT}
@@ -220,6 +220,80 @@ def layer_forward_fp8(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=
         _ptr(y, dt, "y"), C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"),
         ws.numel(), _stream(stream)), "moe_layer_forward_fp8")
     return y
+
+
+def _step_dict(info: MoeCacheStep) -> dict:
+    return {f: getattr(info, f) for f, _ in MoeCacheStep._fields_}
+
+
+class ExpertCache:
+    """An expert cache (moe_cache_*): `slots` experts of the routed weights resident in a device
+    pool, the rest in host memory (w1, w3 [E, I, H] and w2 [E, H, I], bf16 CPU tensors; pin
+    them for asynchronous copies).  The host tensors must outlive the cache."""
+
+    def __init__(self, d: Dims, slots: int, w1, w3, w2, device="cuda"):
+        for name, t in (("w1", w1), ("w3", w3), ("w2", w2)):
+            if t.is_cuda or t.dtype != d.torch_dtype or not t.is_contiguous():
+                raise ValueError(f"{name}: contiguous host tensor of {d.torch_dtype} expected")
+        self._keep = (w1, w3, w2)
+        self.d = d
+        c = d.c()
+        n = int(_lib.lib().moe_cache_pool_bytes(C.byref(c), slots))
+        if n == 0:
+            raise ValueError(f"invalid cache dims {d} / slots {slots}")
+        self.pool = torch.empty(n, dtype=torch.uint8, device=device)
+        h = C.c_void_p()
+        _check(_lib.lib().moe_cache_create(C.byref(c), slots, w1.data_ptr(), w3.data_ptr(),
+                                           w2.data_ptr(), self.pool.data_ptr(), n, C.byref(h)),
+               "moe_cache_create")
+        self.handle = h
+
+    def load(self, experts, copy_stream=None, stream=None) -> dict:
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        info = MoeCacheStep()
+        _check(_lib.lib().moe_cache_load(self.handle, ids.ctypes.data if ids.size else None,
+                                         int(ids.size), _stream(copy_stream), _stream(stream),
+                                         C.byref(info)), "moe_cache_load")
+        return _step_dict(info)
+
+    def slots(self):
+        import numpy as np
+        out = np.empty(self.d.E, np.int32)
+        _check(_lib.lib().moe_cache_slots(self.handle, out.ctypes.data), "moe_cache_slots")
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _lib.lib().moe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def layer_forward_cached(d: Dims, x, wg, bias, cache: ExpertCache, shared=None, y=None, ws=None,
+                         debug=None, stream=None, copy_stream=None):
+    """The fused layer with the routed experts' weights in an ExpertCache; returns (y, step info).
+    Waits for `stream` once, after the routing, to learn which experts are needed."""
+    dt = d.torch_dtype
+    if y is None:
+        y = torch.empty((d.T, d.H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(d, x.device)
+    s1 = s3 = s2 = None
+    if shared is not None:
+        s1, s3, s2 = shared
+    dbg = _debug_struct(debug) if debug else None
+    info = MoeCacheStep()
+    c = d.c()
+    _check(_lib.lib().moe_layer_forward_cached(
+        C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),
+        cache.handle, _ptr(s1, dt, "ws1"), _ptr(s3, dt, "ws3"), _ptr(s2, dt, "ws2"), _ptr(y, dt, "y"),
+        C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream), _stream(copy_stream if copy_stream is not None else stream),
+        C.byref(info)), "moe_layer_forward_cached")
+    return y, _step_dict(info)
 
 
 def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None, debug=None,

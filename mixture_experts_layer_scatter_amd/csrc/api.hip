@@ -7,6 +7,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <vector>
+
 using namespace moe;
 
 namespace {
@@ -194,11 +196,12 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
                    int64_t a_rows, int64_t max_rows, const int32_t* offsets, int G, int G_routed,
                    const ExpertWeights& W, const ExpertWeights* X, void* act, void* out,
                    int32_t* ts_gu, int32_t* ts_dn, int avg_rows, float* tail, hipStream_t s,
-                   void* const* ev = nullptr) {
+                   void* const* ev = nullptr, const int32_t* group_slot = nullptr) {
   const bool bf16 = d->dtype == MOE_BF16;
   // groups past G_routed take the extra weights; there must be some for them, stored like W's
   if (G_routed < 0 || G_routed > G || !W.complete() || (W.fp8() && !bf16)) return hipErrorInvalidValue;
   if (G > G_routed && (!X || !X->complete() || X->fp8() != W.fp8())) return hipErrorInvalidValue;
+  if (group_slot && !bf16) return hipErrorInvalidValue;  // slot indirection: MFMA path only
   int bm_gu, nt_gu, bm_dn, nt_dn;
   if (bf16) {
     gemm_bf16_tiling(GEMM_GATE_UP, avg_rows, I, &bm_gu, &nt_gu);
@@ -235,6 +238,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   gu.G = G;
   gu.G_routed = G_routed;
   gu.tile_start = ts_gu;
+  gu.group_slot = group_slot;
   gu.tail_part = bf16 ? tail : nullptr;
 
   GroupedGemm dn = {};
@@ -256,6 +260,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   dn.G = G;
   dn.G_routed = G_routed;
   dn.tile_start = ts_dn;
+  dn.group_slot = group_slot;
   dn.tail_part = bf16 ? tail : nullptr;
 
   const int cus = num_cus();
@@ -450,12 +455,29 @@ moe_status_t moe_combine(const moe_dims_t* d, const void* y_packed, const int32_
 
 namespace {
 
+// an expert cache the routed weights come from (moe_layer_forward_cached)
+struct CacheUse {
+  moe_expert_cache_t* cache;
+  hipStream_t copy_stream;
+  moe_cache_step_t* info;
+};
+
 moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* wg,
-                                const float* bias, const ExpertWeights& W,
+                                const float* bias, const ExpertWeights& W_in,
                                 const ExpertWeights& SW, void* y, const moe_debug_out_t* dbg,
-                                void* ws, size_t ws_bytes, void* stream) {
+                                void* ws, size_t ws_bytes, void* stream,
+                                const CacheUse* cu = nullptr) {
   moe_status_t st = check_dims(d);
   if (st != MOE_OK) return st;
+  ExpertWeights W = W_in;
+  const int32_t* group_slot = nullptr;
+  if (cu) {
+    if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const CacheView v = cache_view(cu->cache);
+    if (v.E != d->E || v.H != d->H || v.I != d->I) return MOE_ERR_INVALID_ARG;
+    W = ExpertWeights{v.w1, v.w3, v.w2, nullptr, nullptr, nullptr};
+    group_slot = v.table;
+  }
   if (!x || !wg || !W.complete() || !y) {
     if (d->T > 0) return MOE_ERR_INVALID_ARG;
   }
@@ -491,6 +513,19 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
   a.pos = pos;
   a.row_token = row_token;
   MOE_TRY(launch_permute(a, s));
+  if (cu) {
+    // the experts with kept rows must be resident: their counts come back to the host, the
+    // missing ones are copied in on the copy stream and the compute stream waits for them
+    std::vector<int32_t> counts(E), need;
+    MOE_TRY(hipMemcpyAsync(counts.data(), at<int32_t>(ws, L.counts), (size_t)E * 4,
+                           hipMemcpyDeviceToHost, s));
+    MOE_TRY(hipStreamSynchronize(s));
+    for (int e = 0; e < E; ++e)
+      if (counts[e] > 0) need.push_back(e);
+    const moe_status_t ls = moe_cache_load(cu->cache, need.data(), (int32_t)need.size(),
+                                           cu->copy_stream, s, cu->info);
+    if (ls != MOE_OK) return ls;
+  }
   // 4-5. grouped gate-up (rows gathered straight from x) and down
   const int G = E + (fold ? 1 : 0);
   const int64_t max_rows = (int64_t)n + (fold ? T : 0);
@@ -498,7 +533,7 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
   void* yp = at<void>(ws, L.yp);
   MOE_TRY(run_ffn(d, d->I, x, row_token, T, max_rows, offsets, G, E, W, fold ? &SW : nullptr,
                   at<void>(ws, L.act), yp, at<int32_t>(ws, L.ts_gu), at<int32_t>(ws, L.ts_dn), avg,
-                  at<float>(ws, L.tail), s, ev));
+                  at<float>(ws, L.tail), s, ev, group_slot));
   const void* ys = nullptr;
   const int32_t* ys_row0 = nullptr;
   if (fold) {
@@ -551,6 +586,19 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
   return layer_forward_impl(d, x, wg, bias, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr},
                             ExpertWeights{ws1, ws3, ws2, nullptr, nullptr, nullptr}, y, dbg, ws,
                             ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_cached(const moe_dims_t* d, const void* x, const void* wg,
+                                      const float* bias, moe_expert_cache_t* cache,
+                                      const void* ws1, const void* ws3, const void* ws2, void* y,
+                                      const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                      void* stream, void* copy_stream, moe_cache_step_t* info) {
+  if (!cache) return MOE_ERR_INVALID_ARG;
+  if (info) *info = moe_cache_step_t{};
+  const CacheUse cu{cache, (hipStream_t)copy_stream, info};
+  return layer_forward_impl(d, x, wg, bias, ExpertWeights{},
+                            ExpertWeights{ws1, ws3, ws2, nullptr, nullptr, nullptr}, y, dbg, ws,
+                            ws_bytes, stream, &cu);
 }
 
 moe_status_t moe_layer_forward_fp8(const moe_dims_t* d, const void* x, const void* wg,

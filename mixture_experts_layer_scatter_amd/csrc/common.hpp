@@ -98,6 +98,9 @@ struct GroupedGemm {
   const float* b2_scale;
   const float* b_scale_extra;
   const float* b2_scale_extra;
+  // [G_routed] or null: routed group g's weights are matrix group_slot[g] of b / b2 (an expert
+  // cache's slot); null: matrix g (bf16 MFMA path only)
+  const int32_t* group_slot;
   int N, K;                  // output columns, reduction length
   // output C [*, ldc]
   void* c;
@@ -125,6 +128,17 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& g, int max_rows_pe
                             int num_cus, hipStream_t s);
 // bytes of GroupedGemm::tail_part needed by launch_gemm_bf16 for this kind and group size
 size_t gemm_tail_bytes(int avg_rows_per_group);
+
+// cache.hip: the device side of an expert cache (pool slots and the expert -> slot table)
+struct CacheView {
+  const void *w1, *w3, *w2;  // [slots, I, H], [slots, I, H], [slots, H, I]
+  const int32_t* table;      // [E] expert -> slot
+  int E, H, I;
+};
+}  // namespace moe
+struct moe_expert_cache;
+namespace moe {
+CacheView cache_view(const moe_expert_cache* c);
 
 // quant.hip: per-row FP8 E4M3 quantisation of a [rows, K] bf16 or fp32 matrix (K % 8 == 0)
 hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uint8_t* q,

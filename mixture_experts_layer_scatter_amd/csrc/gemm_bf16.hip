@@ -170,6 +170,7 @@ using DecodeShapeFp8 = TileShape<32, 256, 1, 4, 3>;
 
 struct TileLoc {
   int row_base, m0, rows_here, n_t, g;
+  int w;  // index of the group's weights in b / b2 / the scales (its slot when group_slot is set)
 };
 
 // tile `tile` of the (unsplit) tile list: its group, row block and column block
@@ -192,6 +193,9 @@ __device__ __forceinline__ TileLoc locate_tile(const GroupedGemm& p, int tile) {
   const int nblk = li / (mt * GN), rem = li % (mt * GN);
   TileLoc t;
   t.g = g;
+  // a slot of -1 would mean a group with rows whose weights are not resident; the caller rules
+  // that out, and slot 0 keeps the address in range if it ever happened
+  t.w = p.group_slot && g < p.G_routed ? max(p.group_slot[g], 0) : g;
   t.row_base = row_base;
   t.m0 = (rem % mt) * SH::BM;
   t.n_t = nblk * GN + rem / mt;
@@ -235,9 +239,9 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
   float4 sc[TN][4];
   if constexpr (WQ) {
     const bool extra = p.tile_start && t.g >= p.G_routed;
-    const float* s1 = extra ? p.b_scale_extra : p.b_scale + (int64_t)t.g * p.N;
+    const float* s1 = extra ? p.b_scale_extra : p.b_scale + (int64_t)t.w * p.N;
     const float* s2 = EPI != EPI_SWIGLU ? s1
-                      : extra ? p.b2_scale_extra : p.b2_scale + (int64_t)t.g * p.N;
+                      : extra ? p.b2_scale_extra : p.b2_scale + (int64_t)t.w * p.N;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -389,11 +393,12 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     kt0 = __builtin_amdgcn_readfirstlane(t.kt0);
     ktn = __builtin_amdgcn_readfirstlane(t.ktn);
     const bool extra = p.tile_start && t.loc.g >= p.G_routed;
+    const int wsel = __builtin_amdgcn_readfirstlane(t.loc.w);  // uniform: keeps the rsrc scalar
     const char* bbase =
-        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * WB);
+        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)wsel * p.b_stride * WB);
     const char* b2base = bbase;
     if (EPI == EPI_SWIGLU)
-      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)t.loc.g * p.b_stride * WB);
+      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)wsel * p.b_stride * WB);
     const uint32_t b_bytes = (uint32_t)((int64_t)p.N * K * WB);
     rB = make_rsrc(bbase, b_bytes);
     rB2 = make_rsrc(b2base, b_bytes);

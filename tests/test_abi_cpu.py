@@ -117,6 +117,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     src = tmp_path / "layout.c"
     fields = {"moe_dims_t": [f for f, _ in L.MoeDims._fields_],
               "moe_load_stats_t": [f for f, _ in L.MoeLoadStats._fields_],
+              "moe_cache_step_t": [f for f, _ in L.MoeCacheStep._fields_],
               "moe_debug_out_t": [f for f, _ in L.MoeDebugOut._fields_]}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void) {"]
     for st, fs in fields.items():
@@ -131,7 +132,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
     got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
     for st, cls in (("moe_dims_t", L.MoeDims), ("moe_load_stats_t", L.MoeLoadStats),
-                    ("moe_debug_out_t", L.MoeDebugOut)):
+                    ("moe_cache_step_t", L.MoeCacheStep), ("moe_debug_out_t", L.MoeDebugOut)):
         assert got[(st, "size")] == C.sizeof(cls), st
         for f in fields[st]:
             assert got[(st, f)] == getattr(cls, f).offset, (st, f)
@@ -180,3 +181,27 @@ def test_fp8_entry_point_checks():
     args = [p] * 16
     args[10] = None  # shared-expert W1 scales missing
     assert lib.moe_layer_forward_fp8(C.byref(ds), *args, None, p, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_cache_argument_checks():
+    L = _lib()
+    lib = L.lib()
+    p = C.c_void_p(16)  # never dereferenced
+    d = _dims()
+    n = lib.moe_cache_pool_bytes(C.byref(d), 4)
+    assert n > 3 * 4 * 128 * 128 * 2 and n % 256 == 0
+    assert lib.moe_cache_pool_bytes(C.byref(d), 0) == 0
+    assert lib.moe_cache_pool_bytes(C.byref(_dims(dtype=L.MOE_F32)), 4) == 0
+    out = C.c_void_p(123)
+    assert lib.moe_cache_create(C.byref(d), 4, p, p, p, p, n, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_create(C.byref(d), 0, p, p, p, p, n, C.byref(out)) == L.MOE_ERR_INVALID_ARG
+    assert out.value is None  # cleared on failure
+    assert lib.moe_cache_create(C.byref(d), 4, None, p, p, p, n, C.byref(out)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_create(C.byref(d), 4, p, p, p, p, n - 1, C.byref(out)) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_cache_create(C.byref(_dims(dtype=L.MOE_F32)), 4, p, p, p, p, n,
+                                C.byref(out)) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_cache_load(None, None, 0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_slots(None, p) == L.MOE_ERR_INVALID_ARG
+    lib.moe_cache_destroy(None)  # no-op
+    assert lib.moe_layer_forward_cached(C.byref(d), p, p, None, None, None, None, None, p, None,
+                                        p, 1 << 40, None, None, None) == L.MOE_ERR_INVALID_ARG

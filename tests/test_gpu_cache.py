@@ -1,0 +1,115 @@
+"""GPU checks of the expert cache (moe_cache_*, moe_layer_forward_cached).
+
+* Residency: every batch's hits, loads and evictions and the expert -> slot table equal the
+  oracle's LRU model (oracle/cache.py) step for step, and each resident slot holds its expert's
+  weights bit for bit.
+* Layer: the cached layer's output equals moe_layer_forward's bit for bit (the same kernels
+  read the same weight values from other addresses), over a sequence of batches whose routing
+  changes, with evictions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from gpu_util import bf16_normal, bits, dev, log, need_gpu
+from oracle.cache import LRUCache
+
+pytestmark = pytest.mark.gpu
+
+import mixture_experts_layer_scatter_amd as moe
+
+
+def _pinned(a):
+    t = torch.empty(a.shape, dtype=torch.bfloat16, pin_memory=True)
+    t.copy_(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16))
+    return t
+
+
+def _host_weights(rng, E, H, I):
+    W1 = bf16_normal(rng, (E, I, H), 1 / np.sqrt(H))
+    W3 = bf16_normal(rng, (E, I, H), 1 / np.sqrt(H))
+    W2 = bf16_normal(rng, (E, H, I), 1 / np.sqrt(I))
+    return W1, W3, W2
+
+
+@pytest.mark.parametrize("E,slots,zipf", [(16, 5, 1.0), (64, 20, 1.2)])
+def test_residency_matches_lru_model(E, slots, zipf):
+    need_gpu()
+    log(f"cache residency E={E} slots={slots}")
+    rng = np.random.default_rng(E)
+    H, I = 64, 64
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    d = moe.Dims(T=1, H=H, E=E, k=1, I=I)
+    cache = moe.ExpertCache(d, slots, _pinned(W1), _pinned(W3), _pinned(W2))
+    ref = LRUCache(E, slots)
+    p = np.arange(1, E + 1, dtype=np.float64) ** -zipf
+    p /= p.sum()
+    copy = torch.cuda.Stream()
+    for step in range(60):
+        req = rng.choice(E, int(rng.integers(1, slots + 1)), replace=False, p=p).tolist()
+        req = req + req[:1]  # a duplicate id is allowed
+        info = cache.load(req, copy_stream=copy)
+        hits, loads, ev = ref.request(req)
+        assert (info["hits"], info["loads"], info["evictions"]) == (len(hits), len(loads), len(ev)), step
+        assert info["requested"] == len(set(req))
+        assert info["bytes_loaded"] == len(loads) * (3 * H * I * 2)
+        assert cache.slots().tolist() == ref.slot_of, step
+    torch.cuda.synchronize()
+    # the pool holds each resident expert's weights at its slot
+    pool = cache.pool
+    n13 = slots * I * H * 2
+    w1p = pool[:n13].view(torch.int16).view(slots, I, H)
+    w3p = pool[_align(n13):_align(n13) + n13].view(torch.int16).view(slots, I, H)
+    for e, s in enumerate(cache.slots()):
+        if s >= 0:
+            assert np.array_equal(w1p[s].cpu().numpy().view(np.uint16), W1[e])
+            assert np.array_equal(w3p[s].cpu().numpy().view(np.uint16), W3[e])
+    with pytest.raises(moe.MoeError):
+        cache.load(list(range(slots + 1)))  # more experts than slots
+    cache.close()
+
+
+def _align(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("E,slots,T,k,shared", [(16, 6, 3, 2, 0), (64, 16, 8, 2, 128),
+                                               (32, 10, 5, 2, 256)])
+def test_cached_layer_bit_exact(E, slots, T, k, shared):
+    need_gpu()
+    log(f"cached layer E={E} slots={slots} T={T} k={k} shared={shared}")
+    rng = np.random.default_rng(E * 7 + T)
+    H, I = 256, 128
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    wg = bf16_normal(rng, (E, H), 1 / np.sqrt(H))
+    bias = (-0.5 * np.log(rng.permutation(E) + 1.0)).astype(np.float32)  # skewed popularity
+    d = moe.Dims(T=T, H=H, E=E, k=k, I=I, I_shared=shared)
+    sh = None
+    if shared:
+        sh = tuple(dev(a) for a in (bf16_normal(rng, (shared, H), 1 / np.sqrt(H)),
+                                    bf16_normal(rng, (shared, H), 1 / np.sqrt(H)),
+                                    bf16_normal(rng, (H, shared), 1 / np.sqrt(shared))))
+    cache = moe.ExpertCache(d, slots, _pinned(W1), _pinned(W3), _pinned(W2))
+    dw1, dw3, dw2, dwg, dbias = dev(W1), dev(W3), dev(W2), dev(wg), dev(bias)
+    ref = LRUCache(E, slots)
+    copy = torch.cuda.Stream()
+    ws = moe.workspace(d)
+    total = dict(hits=0, loads=0, evictions=0)
+    for step in range(16):
+        x = dev(bf16_normal(rng, (T, H)))
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        y_ref = moe.layer_forward(d, x, dwg, dbias, dw1, dw3, dw2, sh, ws=ws)
+        y, info = moe.layer_forward_cached(d, x, dwg, dbias, cache, sh, ws=ws,
+                                           debug=dict(counts=counts), copy_stream=copy)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), bits(y_ref)), step
+        need = np.nonzero(counts.cpu().numpy())[0].tolist()
+        hits, loads, ev = ref.request(need)
+        assert (info["hits"], info["loads"], info["evictions"]) == (len(hits), len(loads), len(ev))
+        assert cache.slots().tolist() == ref.slot_of
+        for key in total:
+            total[key] += info[key]
+    log(f"  over 16 batches: {total}")
+    assert total["evictions"] > 0 and total["hits"] > 0
+    cache.close()
