@@ -198,7 +198,8 @@ def main():
         shape = "TileShape<256,256,2,4,2>"
         rows = "256x256 tiles"
     else:
-        shape = "TileShape<32,256,1,4,3>" if fp8 else "TileShape<32,256,1,4,4>"
+        shape = (("TileShape<32,256,1,4,2,128>" if w.H % 128 == 0 else "TileShape<32,256,1,4,3>")
+                 if fp8 else "TileShape<32,256,1,4,4>")
         rows = "32-row tiles"
     roof["kernel"] = (f"gemm_kernel<{shape}, SwiGLU{', FP8 weights' if fp8 else ''}> + "
                       f"gemm_tail_kernel (grouped gate-up, {rows})")

@@ -59,8 +59,6 @@ namespace moe {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kBK = 64;         // k elements per step
-constexpr int kRowBytes = 128;  // one LDS row of a k-step
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -105,12 +103,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
-// swizzle of the 16-byte chunks of a 128-byte LDS row: distinct banks for the 8 (and the 16)
-// consecutive rows that one fragment read serves per cycle
-__device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-// the same for the 64-byte rows of an FP8 weight tile (four 16-byte chunks); it depends on
-// bits 1..4 of the row only, so a fragment's rows (32 apart) share it
-__device__ __forceinline__ int row_swizzle4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Swizzle of the 16-byte chunks of an LDS row of CH chunks (chunk c of row r sits at c ^
+// swizzle(r)): the 8 (and the 16) consecutive rows that one fragment read serves per cycle fall
+// in distinct banks.  It depends on bits 0..4 of the row only, so the rows of a fragment's
+// 32-row blocks share it.
+template <int CH>
+__device__ __forceinline__ int row_swizzle(int r) {
+  static_assert(CH == 4 || CH == 8 || CH == 16, "rows of 64, 128 or 256 bytes");
+  if constexpr (CH == 16) return r & 15;
+  else if constexpr (CH == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
 // eight E4M3 codes -> eight bf16 values (exact: the upper half of each fp32 conversion)
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 v) {
@@ -129,16 +132,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 v) {
   return r.h;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int S_>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_ = 64>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int BK = BK_;                      // k elements per LDS stage
+  static constexpr int ROWB = BK * 2, CH = ROWB / 16; // bytes and 16-byte chunks of an A row
   static constexpr int WAVES = WM * WN, THREADS = WAVES * kWave;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wavefront tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32 x 32 MFMA blocks per wavefront
-  static constexpr int KK = kBK / 16;                 // MFMA k-steps per LDS stage
-  static constexpr int RPL = 1024 / kRowBytes;        // A rows one 1 KB wavefront load covers
+  static constexpr int KK = BK / 16;                  // MFMA k-steps per LDS stage
+  static constexpr int RPL = 1024 / ROWB;             // A rows one 1 KB wavefront load covers
   static constexpr int A_LOADS = BM / RPL / WAVES;
-  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int A_BYTES = BM * ROWB;
+  static_assert(BK == 64 || BK == 128, "k-step");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wavefront tile is a multiple of 32 x 32");
   static_assert(A_LOADS * RPL * WAVES == BM, "load split");
 };
@@ -146,7 +152,8 @@ struct TileShape {
 // LDS geometry of a shape with bf16 (WQ = false) or E4M3 (WQ = true) weights
 template <class SH, bool WQ>
 struct Geo {
-  static constexpr int B_ROWB = WQ ? kBK : kRowBytes;  // bytes of one weight row of a k-step
+  static constexpr int B_ROWB = WQ ? SH::BK : SH::ROWB;  // bytes of one weight row of a stage
+  static constexpr int B_CH = B_ROWB / 16;            // its 16-byte chunks
   static constexpr int B_RPL = 1024 / B_ROWB;         // weight rows one 1 KB load covers
   static constexpr int B_LOADS = SH::BN / B_RPL / SH::WAVES;
   static constexpr int L = SH::A_LOADS + B_LOADS;     // loads per wavefront per stage
@@ -159,12 +166,15 @@ struct Geo {
 
 using PrefillShape = TileShape<256, 256, 2, 4, 2>;
 using DecodeShape = TileShape<32, 256, 1, 4, 4>;
-// FP8 weights halve the weight tile.  Decode: three 20 KB stages leave room for two workgroups
-// per CU (eight wavefronts with their loads in flight), which streams the weights faster than
-// one workgroup with seven stages (measured: 1.50 against 2.09 ms for the DeepSeek-shaped
-// gate-up).  Prefill: two stages, as for bf16 (a third stage measured slower).
+// FP8 weights halve the weight tile.  Decode: stages of 128 k (each weight row a whole 128-byte
+// line; with 64 k every line was fetched in two halves a k-step apart), two of them so that two
+// workgroups fit per CU (eight wavefronts with loads in flight).  Measured on the DeepSeek-shaped
+// gate-up: 1.35 ms, against 1.51 ms with 64-k stages (three, two workgroups), 1.86 ms with three
+// 128-k stages (one workgroup) and 2.09 ms with seven 64-k stages (one workgroup).  The 64-k
+// shape serves K not divisible by 128.  Prefill: two 64-k stages, as for bf16.
 using PrefillShapeFp8 = TileShape<256, 256, 2, 4, 2>;
 using DecodeShapeFp8 = TileShape<32, 256, 1, 4, 3>;
+using DecodeShapeFp8K128 = TileShape<32, 256, 1, 4, 2, 128>;
 
 // ---- tile bookkeeping shared by the GEMM and its tail reduction ---------------------------------
 
@@ -333,14 +343,15 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   using GE = Geo<SH, WQ>;
   constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, L = GE::L;
   constexpr int TM = SH::TM, TN = SH::TN, KK = SH::KK, RPL = SH::RPL;
-  constexpr int B_ROWB = GE::B_ROWB, B_RPL = GE::B_RPL, B_LOADS = GE::B_LOADS;
+  constexpr int B_ROWB = GE::B_ROWB, B_RPL = GE::B_RPL, B_LOADS = GE::B_LOADS, B_CH = GE::B_CH;
+  constexpr int ROWB = SH::ROWB, CH = SH::CH;
   constexpr int STAGE = GE::STAGE, WB = WQ ? 1 : 2;  // weight bytes per element
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs W1 and W3 blocks");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wid / WN, wn = wid % WN;
-  const int K = p.K, KT = K / kBK;
+  const int K = p.K, KT = K / SH::BK;
   const int NT = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int total_base = p.tile_start ? p.tile_start[p.G] : (p.static_rows + BM - 1) / BM * NT;
   // split-K: ksplit consecutive copies of the tile list; copy ks reduces over its share of the
@@ -352,8 +363,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * 2));
 
   const int l32 = lane & 31, hi = lane >> 5;
-  const int sw = row_swizzle(l32), sw4 = row_swizzle4(l32);
-  const uint32_t a_frag = (uint32_t)((wm * SH::WTM + l32) * kRowBytes);
+  const int sw = row_swizzle<CH>(l32), swb = row_swizzle<B_CH>(l32);
+  const uint32_t a_frag = (uint32_t)((wm * SH::WTM + l32) * ROWB);
   const uint32_t b_frag = (uint32_t)(SH::A_BYTES + (wn * SH::WTN + l32) * B_ROWB);
 
   struct Tile {
@@ -404,8 +415,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     rB2 = make_rsrc(b2base, b_bytes);
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i) {
-      const int r = (wid * SH::A_LOADS + i) * RPL + lane / 8;
-      const int c = (lane & 7) ^ row_swizzle(r);
+      const int r = (wid * SH::A_LOADS + i) * RPL + lane / CH;
+      const int c = (lane % CH) ^ row_swizzle<CH>(r);
       uint32_t off = kOutOfRange;
       if (r < t.loc.rows_here) {
         const int prow = t.loc.row_base + t.loc.m0 + r;
@@ -417,8 +428,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       // lane: weight row lane / (chunks per row), chunk lane % (chunks per row)
-      const int n = (wid * B_LOADS + i) * B_RPL + (WQ ? lane / 4 : lane / 8);
-      const int c = WQ ? (lane & 3) ^ row_swizzle4(n) : (lane & 7) ^ row_swizzle(n);
+      const int n = (wid * B_LOADS + i) * B_RPL + lane / B_CH;
+      const int c = (lane % B_CH) ^ row_swizzle<B_CH>(n);
       const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
       b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * WB + c * 16 : kOutOfRange;
     }
@@ -428,7 +439,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     const bool valid = lk < ktn;
     char* sa = smem + slot * STAGE;
     char* sb = sa + SH::A_BYTES;
-    const int kb = valid ? (kt0 + lk) * kRowBytes : 0;
+    const int kb = valid ? (kt0 + lk) * ROWB : 0;
     const int kbw = valid ? (kt0 + lk) * B_ROWB : 0;
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i)
@@ -450,16 +461,17 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   auto read_frags = [&](const char* st, int kk, int buf) {
     const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 32 * kRowBytes);
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 32 * ROWB);
     if constexpr (WQ) {
-      // 8 codes = half of the 16-byte chunk kk of the 64-byte row
-      const uint32_t woff = (uint32_t)(((kk ^ sw4) * 16) + hi * 8);
+      // a k-sub's 16 codes are chunk kk of the row; the lane takes half of it
+      const uint32_t woff = (uint32_t)(((kk ^ swb) * 16) + hi * 8);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         fb[buf][j] = fp8x8_to_bf16(*(const uint2*)(st + b_frag + woff + j * 32 * B_ROWB));
     } else {
+      const uint32_t boff = (uint32_t)(((kk * 2 + hi) ^ swb) * 16);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + coff + j * 32 * kRowBytes);
+      for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + boff + j * 32 * B_ROWB);
     }
   };
   // weights as the first operand: D[column][token]
@@ -557,7 +569,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, i
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wid / SH::WN, wn = wid % SH::WN;
   const int xcd = blockIdx.x % 8, t = (blockIdx.x / 8) % kTailPieces, ib = blockIdx.x / (8 * kTailPieces);
-  const TailPlan plan = tail_plan(p.tile_start[p.G], xcd, nx, p.K / kBK, true);
+  const TailPlan plan = tail_plan(p.tile_start[p.G], xcd, nx, p.K / SH::BK, true);
   if (plan.pieces <= 1 || t >= plan.tail) return;
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -664,10 +676,14 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
       if (big)
         return gather ? run<PrefillShapeFp8, EPI_SWIGLU, true, 8, true>(p, mt, num_cus, s)
                       : run<PrefillShapeFp8, EPI_SWIGLU, false, 8, true>(p, mt, num_cus, s);
+      if (p.K % 128 == 0)
+        return gather ? run<DecodeShapeFp8K128, EPI_SWIGLU, true, 1, true>(p, mt, num_cus, s)
+                      : run<DecodeShapeFp8K128, EPI_SWIGLU, false, 1, true>(p, mt, num_cus, s);
       return gather ? run<DecodeShapeFp8, EPI_SWIGLU, true, 1, true>(p, mt, num_cus, s)
                     : run<DecodeShapeFp8, EPI_SWIGLU, false, 1, true>(p, mt, num_cus, s);
     }
     if (big) return run<PrefillShapeFp8, EPI_BF16, false, 8, true>(p, mt, num_cus, s);
+    if (p.K % 128 == 0) return run<DecodeShapeFp8K128, EPI_BF16, false, 1, true>(p, mt, num_cus, s);
     return run<DecodeShapeFp8, EPI_BF16, false, 1, true>(p, mt, num_cus, s);
   }
   if (kind == GEMM_GATE_UP) {
