@@ -47,6 +47,14 @@ def lib():
         L.oracle_quantize_fp8.argtypes = [_i64, _i64, C.c_int, _p, _p, _p]
         L.oracle_dequantize_fp8.restype = None
         L.oracle_dequantize_fp8.argtypes = [_i64, _i64, _p, _p, _p]
+        L.oracle_fp4_decode.restype = C.c_double
+        L.oracle_fp4_decode.argtypes = [C.c_uint8]
+        L.oracle_fp4_encode.restype = C.c_uint8
+        L.oracle_fp4_encode.argtypes = [C.c_float]
+        L.oracle_quantize_mxfp4.restype = None
+        L.oracle_quantize_mxfp4.argtypes = [_i64, _i64, C.c_int, _p, _p, _p]
+        L.oracle_dequantize_mxfp4.restype = None
+        L.oracle_dequantize_mxfp4.argtypes = [_i64, _i64, _p, _p, _p]
         L.oracle_load_stats.restype = None
         L.oracle_load_stats.argtypes = [_i64, _i64, _i64, _i32, _p, _p, _p, _p, _p]
         L.oracle_permute.restype = _i64
@@ -185,6 +193,35 @@ def dequantize_fp8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     K = q.shape[-1]
     out = np.empty(q.shape, np.float64)
     lib().oracle_dequantize_fp8(q.size // K if K else 0, K, _ptr(q), _ptr(scales), _ptr(out))
+    return out
+
+
+def fp4_decode(code: int) -> float:
+    return float(lib().oracle_fp4_decode(int(code)))
+
+
+def fp4_encode(x: float) -> int:
+    return int(lib().oracle_fp4_encode(float(x)))
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """MXFP4 quantisation of a [..., K] bf16-bits or float32 matrix (K % 32 == 0).  Returns
+    (codes uint8 [..., K/2], two per byte, low nibble first; scales uint8 [..., K/32], E8M0)."""
+    w = _c(w)
+    K = w.shape[-1]
+    rows = w.size // K if K else 0
+    q = np.empty(w.shape[:-1] + (K // 2,), np.uint8)
+    sc = np.empty(w.shape[:-1] + (K // 32,), np.uint8)
+    lib().oracle_quantize_mxfp4(rows, K, _dt(w), _ptr(w), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def dequantize_mxfp4(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.uint8)
+    K = q.shape[-1] * 2
+    out = np.empty(q.shape[:-1] + (K,), np.float64)
+    lib().oracle_dequantize_mxfp4(q.size * 2 // K if K else 0, K, _ptr(q), _ptr(scales), _ptr(out))
     return out
 
 

@@ -77,6 +77,72 @@ void oracle_quantize_fp8(int64_t rows, int64_t K, int dt, const void* w, uint8_t
     }
 }
 
+double oracle_fp4_decode(uint8_t c) {
+    int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    /* subnormal: m/2 * 2^(1-1); normal: (1 + m/2) * 2^(e-1) */
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+uint8_t oracle_fp4_encode(float x) {
+    uint8_t sign = signbit(x) ? 8 : 0;
+    double a = fabs((double)x);
+    if (a >= 6.0) return sign | 7; /* saturate */
+    /* the quantum is 0.5 below 2, 1 in [2, 4), 2 in [4, 6] */
+    double quantum = a < 2.0 ? 0.5 : a < 4.0 ? 1.0 : 2.0;
+    double v = nearbyint(a / quantum) * quantum; /* ties to even multiples */
+    /* codes in increasing value: 0, 0.5, 1, 1.5, 2, 3, 4, 6 */
+    static const double vals[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    uint8_t code = 0;
+    for (uint8_t c = 0; c < 8; ++c)
+        if (vals[c] == v) code = c;
+    return sign | code;
+}
+
+void oracle_quantize_mxfp4(int64_t rows, int64_t K, int dt, const void* w, uint8_t* q,
+                           uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            double amax = 0.0;
+            for (int64_t i = 0; i < 32; ++i) {
+                double a = fabs(ld(dt, w, r * K + b * 32 + i));
+                if (a > amax) amax = a;
+            }
+            int shared = 0;
+            uint8_t sc = 127;
+            if (amax > 0.0) {
+                int E;
+                frexp(amax, &E); /* amax = f * 2^E, f in [0.5, 1): floor(log2(amax)) = E - 1 */
+                shared = E - 1 - 2;
+                if (shared < -126) shared = -126;
+                if (shared > 127) shared = 127;
+                sc = (uint8_t)(shared + 127);
+            }
+            scales[r * (K / 32) + b] = sc;
+            for (int64_t i = 0; i < 32; i += 2) {
+                uint8_t c0 = 0, c1 = 0;
+                if (amax > 0.0) {
+                    c0 = oracle_fp4_encode((float)ldexp(ld(dt, w, r * K + b * 32 + i), -shared));
+                    c1 = oracle_fp4_encode((float)ldexp(ld(dt, w, r * K + b * 32 + i + 1), -shared));
+                }
+                q[(r * K + b * 32 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+}
+
+void oracle_dequantize_mxfp4(int64_t rows, int64_t K, const uint8_t* q, const uint8_t* scales,
+                             double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = q[(r * K + k) / 2];
+            uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15);
+            out[r * K + k] = oracle_fp4_decode(code) * ldexp(1.0, (int)scales[r * (K / 32) + k / 32] - 127);
+        }
+}
+
 void oracle_dequantize_fp8(int64_t rows, int64_t K, const uint8_t* q, const float* scales,
                            double* out) {
 #pragma omp parallel for schedule(static)

@@ -60,6 +60,28 @@ void oracle_quantize_fp8(int64_t rows, int64_t K, int dt, const void* w, uint8_t
 void oracle_dequantize_fp8(int64_t rows, int64_t K, const uint8_t* q, const float* scales,
                            double* out);
 
+/* FP4 E2M1 (the OCP microscaling element format: 1 sign, 2 exponent bits with bias 1, 1
+ * mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN).
+ * fp4_decode: value of a 4-bit code; fp4_encode: the nearest code, ties to the even code,
+ * |x| > 6 saturating to +-6. */
+double oracle_fp4_decode(uint8_t code);
+uint8_t oracle_fp4_encode(float x);
+
+/* MXFP4 weight quantisation (the OCP microscaling format's MXFP4: blocks of 32 consecutive
+ * elements along K share one E8M0 scale 2^(s - 127)), a reading of [P3] §5.2's 4-bit expert
+ * weights.  Per block: amax = max |w|; if amax == 0 the scale code is 127 (scale 1) and every
+ * code 0; else e = floor(log2(amax)), shared = clamp(e - 2, -126, 127) (2 = the largest
+ * exponent of E2M1, as the format's rule sets it; the clamp keeps the scale a normal float),
+ * scale code = shared + 127, and q = fp4_encode(w / 2^shared) (exact division).  K % 32 == 0.
+ * q [rows, K/2]: element 2j in the low nibble of byte j, 2j + 1 in the high nibble;
+ * scales [rows, K/32]. */
+void oracle_quantize_mxfp4(int64_t rows, int64_t K, int dt, const void* w, uint8_t* q,
+                           uint8_t* scales);
+
+/* out[r,k] = fp4_decode(code of (r,k)) * 2^(scales[r, k/32] - 127), exact in float64. */
+void oracle_dequantize_mxfp4(int64_t rows, int64_t K, const uint8_t* q, const uint8_t* scales,
+                             double* out);
+
 /* Expert capacity, [P3] §2.1 (router sketch, capacity = tokens / experts x
  * factor), with the top-k factor included: floor(T*k/E*factor) in double. */
 int32_t oracle_capacity(int32_t T, int32_t k, int32_t E, double factor);

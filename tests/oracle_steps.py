@@ -46,6 +46,23 @@ def fp8_dequantised(a):
     return oracle.dequantize_fp8(q, s)
 
 
+class Mxfp4Weights(Weights):
+    """The same experts quantised to MXFP4 by the oracle, returned dequantised (float64)."""
+
+    def expert(self, e):
+        if e in self._e:
+            return self._e[e]
+        t = tuple(mxfp4_dequantised(a) for a in moe_synth.expert_weights(self.w, e))
+        if self.cache:
+            self._e[e] = t
+        return t
+
+
+def mxfp4_dequantised(a):
+    q, s = oracle.quantize_mxfp4(a)
+    return oracle.dequantize_mxfp4(q, s)
+
+
 def routing(w: moe_synth.Workload, x=None, logits=None):
     """Oracle gate (unless logits are given), route and permute for workload w."""
     if logits is None:
