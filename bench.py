@@ -35,9 +35,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--weights", choices=("same", "fp8"), default="same",
-                    help="expert weights in the layer's storage type, or FP8 E4M3 with per-row "
-                         "scales (quantised once before timing; bf16 layers)")
+    ap.add_argument("--weights", choices=("same", "fp8", "mxfp4"), default="same",
+                    help="expert weights in the layer's storage type, FP8 E4M3 with per-row "
+                         "scales, or MXFP4 (quantised once before timing; bf16 layers)")
     ap.add_argument("--cache-slots", type=int, default=0,
                     help="also measure the layer with its routed experts in an HBM expert cache "
                          "of this many slots, filled from pinned host memory (cold and warm)")
@@ -82,32 +82,36 @@ def main():
     sh = stream.cuda_stream
 
     fp8 = args.weights == "fp8"
+    mx = args.weights == "mxfp4"
+    lowbit = fp8 or mx
     quant_err = None
-    if fp8:
+    if lowbit:
         if w.dtype != "bf16":
-            sys.exit("--weights fp8 needs a bf16 workload")
+            sys.exit(f"--weights {args.weights} needs a bf16 workload")
         # reference output with the bf16 weights, then quantise and drop them
         moe.layer_forward(d, t["x"], t["wg"], t["bias"], t["w1"], t["w3"], t["w2"], t["shared"],
                           y=y, ws=ws)
         y_ref = y.float().clone()
-        q = {k: moe.quantize_fp8(t[k]) for k in ("w1", "w3", "w2")}
-        q_sh = None if t["shared"] is None else tuple(moe.quantize_fp8(a) for a in t["shared"])
+        quant = moe.quantize_mxfp4 if mx else moe.quantize_fp8
+        q = {k: quant(t[k]) for k in ("w1", "w3", "w2")}
+        q_sh = None if t["shared"] is None else tuple(quant(a) for a in t["shared"])
         torch.cuda.synchronize()
         for k in ("w1", "w3", "w2"):
             t[k] = None
         t["shared"] = None
         torch.cuda.empty_cache()
-        log("expert weights quantised to FP8 E4M3 (per-row scales)")
+        log("expert weights quantised to " + ("MXFP4" if mx else "FP8 E4M3 (per-row scales)"))
 
     def step(debug=None):
-        if fp8:
-            moe.layer_forward_fp8(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"], q["w2"], q_sh,
-                                  y=y, ws=ws, debug=debug)
+        if lowbit:
+            fwd = moe.layer_forward_mxfp4 if mx else moe.layer_forward_fp8
+            fwd(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"], q["w2"], q_sh, y=y, ws=ws,
+                debug=debug)
         else:
             moe.layer_forward(d, t["x"], t["wg"], t["bias"], t["w1"], t["w3"], t["w2"],
                               t["shared"], y=y, ws=ws, debug=debug)
 
-    if fp8:
+    if lowbit:
         step()
         torch.cuda.synchronize()
         quant_err = float(torch.linalg.vector_norm(y.float() - y_ref) / torch.linalg.vector_norm(y_ref))
@@ -165,12 +169,13 @@ def main():
     load["ms"] = round(e0.elapsed_ms(e1) / n_ls, 4)
 
     cache_res = None
-    if args.cache_slots > 0 and not fp8:
+    if args.cache_slots > 0 and not lowbit:
         cache_res = measure_cache(moe, d, t, args.cache_slots, ms_per_step, log)
 
     es = 2 if w.dtype == "bf16" else 4
-    wes = 1 if fp8 else es                      # bytes of one expert weight element
-    sc = lambda rows: 4.0 * rows if fp8 else 0.0  # per-row scales of FP8 weights
+    # bytes of one expert weight element, and of the scales of a [rows, K] weight
+    wes = 1 if fp8 else 0.5 + 1.0 / 32 if mx else es
+    sc = lambda rows: 4.0 * rows if fp8 else 0.0
     Is = w.I_shared
     F = 2.0 * w.T * w.H * w.E + 6.0 * R * w.H * w.I + 6.0 * w.T * w.H * Is
     B = (3.0 * w.H * w.I * wes * touched + sc((2 * w.I + w.H) * touched)
@@ -191,18 +196,21 @@ def main():
         achieved = gu_flops / (gu_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["traffic"] = profiled_traffic(w.name + ("_fp8" if fp8 else ""))
+    roof["traffic"] = profiled_traffic(w.name + ("_fp8" if fp8 else "_mxfp4" if mx else ""))
     # the library takes 256-row tiles when a group holds >= 128 rows on average
     # (the timed span is the grouped GEMM plus the reduction of its split last round of tiles)
-    if (w.T * w.k) // w.E >= 128:
+    if mx:
+        shape, rows = "TileShape<32,256,1,4,3,128>", "32-row tiles"
+    elif (w.T * w.k) // w.E >= 128:
         shape = "TileShape<256,256,2,4,2>"
         rows = "256x256 tiles"
     else:
         shape = (("TileShape<32,256,1,4,2,128>" if w.H % 128 == 0 else "TileShape<32,256,1,4,3>")
                  if fp8 else "TileShape<32,256,1,4,4>")
         rows = "32-row tiles"
-    roof["kernel"] = (f"gemm_kernel<{shape}, SwiGLU{', FP8 weights' if fp8 else ''}> + "
-                      f"gemm_tail_kernel (grouped gate-up, {rows})")
+    tag = ", FP8 weights" if fp8 else ", MXFP4 weights" if mx else ""
+    roof["kernel"] = (f"gemm_kernel<{shape}, SwiGLU{tag}> + gemm_tail_kernel "
+                      f"(grouped gate-up, {rows})")
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
     layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
@@ -223,7 +231,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "I_shared": Is, "capacity": cap, "accumulate": "fp32",
                    **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {}),
-                   **({"expert_weights": "fp8_e4m3_per_row_scale"} if fp8 else {})},
+                   **({"expert_weights": "fp8_e4m3_per_row_scale"} if fp8 else {}),
+                   **({"expert_weights": "mxfp4_e2m1_e8m0_per_32"} if mx else {})},
         "roofline": roof,
         "layer": {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
                   "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
@@ -231,7 +240,7 @@ def main():
                   "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
                   "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
                   "load_stats": load,
-                  **({"fp8_vs_bf16_weights_rel_l2": round(quant_err, 5)} if fp8 else {}),
+                  **({"lowbit_vs_bf16_weights_rel_l2": round(quant_err, 5)} if lowbit else {}),
                   **({"expert_cache": cache_res} if cache_res is not None else {})},
     }
 

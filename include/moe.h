@@ -234,6 +234,31 @@ moe_status_t moe_load_stats(const moe_dims_t* dims, const int32_t* topk_ids, int
 moe_status_t moe_quantize_fp8(int64_t rows, int32_t K, int32_t dtype, const void* w, uint8_t* q,
                               float* scales, void* stream);
 
+/* MXFP4 weight quantisation: E2M1 codes (OCP microscaling: sign, 2 exponent bits
+ * with bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0
+ * scale 2^(s - 127) per 32 consecutive elements of a row, a reading of [P3]
+ * §5.2's 4-bit expert weights (weight-only here; activations stay bf16).
+ *  w [rows, K] of storage `dtype` (MOE_BF16 or MOE_F32), K % 32 == 0.
+ *  Per block of 32: amax = max |w|; 0 gives scale code 127 and codes 0; else
+ *  shared = clamp(floor(log2(amax)) - 2, -126, 127), scale code = shared + 127,
+ *  and each code the E2M1 value nearest to w / 2^shared (ties to even,
+ *  saturating at +-6).
+ *  q [rows, K/2] u8: element 2j in the low nibble of byte j; scales
+ *  [rows, K/32] u8.  Quantise w1 and w3 as [E*I, H] and w2 as [E*H, I]. */
+moe_status_t moe_quantize_mxfp4(int64_t rows, int32_t K, int32_t dtype, const void* w,
+                                uint8_t* q, uint8_t* scales, void* stream);
+
+/* moe_expert_ffn with MXFP4 weights (codes and scales as moe_quantize_mxfp4
+ * writes them; w1/w3 scales [E*I, H/32], w2 scales [E*H, I/32]).  dims->dtype
+ * must be MOE_BF16, H and I multiples of 128.  The codes widen, times their
+ * block scale, exactly to bf16 for the MFMA.  Every group size runs on the
+ * 32-row tiles (the weight-streaming shape). */
+moe_status_t moe_expert_ffn_mxfp4(const moe_dims_t* dims, const void* x_packed,
+                                  const int32_t* offsets, const uint8_t* w1q, const uint8_t* w1s,
+                                  const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                  const uint8_t* w2s, void* y_packed, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* moe_expert_ffn with FP8 weights: w1q/w3q [E,I,H], w2q [E,H,I] E4M3 codes
  * and their per-row scales w1s/w3s [E*I], w2s [E*H] (as moe_quantize_fp8
  * writes them).  dims->dtype must be MOE_BF16 (x_packed, y_packed bf16).
@@ -258,6 +283,19 @@ moe_status_t moe_layer_forward_fp8(const moe_dims_t* dims, const void* x, const 
                                    const uint8_t* ws3q, const float* ws3s, const uint8_t* ws2q,
                                    const float* ws2s, void* y, const moe_debug_out_t* dbg,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward with MXFP4 expert weights (the gate stays bf16), as
+ * moe_layer_forward_fp8 with E8M0 block scales in place of the per-row fp32
+ * scales; the shared expert's weights likewise.  dims->dtype must be
+ * MOE_BF16; H, I and I_shared multiples of 128. */
+moe_status_t moe_layer_forward_mxfp4(const moe_dims_t* dims, const void* x, const void* wg,
+                                     const float* bias, const uint8_t* w1q, const uint8_t* w1s,
+                                     const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                     const uint8_t* w2s, const uint8_t* ws1q, const uint8_t* ws1s,
+                                     const uint8_t* ws3q, const uint8_t* ws3s,
+                                     const uint8_t* ws2q, const uint8_t* ws2s, void* y,
+                                     const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* ---- Expert cache: experts resident in HBM up to a number of slots ----------
  * [P3] §3.2 keeps a subset of the experts in HBM and loads the others from

@@ -174,6 +174,63 @@ def quantize_fp8(w, q=None, scales=None, stream=None):
     return q, scales
 
 
+def quantize_mxfp4(w, q=None, scales=None, stream=None):
+    """MXFP4 quantisation of a bf16 or fp32 device tensor [..., K] (K % 32 == 0).  Returns (codes
+    uint8 [..., K/2], two per byte, low nibble first; E8M0 scales uint8 [..., K/32])."""
+    dt = {torch.bfloat16: _lib.MOE_BF16, torch.float32: _lib.MOE_F32}.get(w.dtype)
+    if dt is None:
+        raise TypeError(f"quantize_mxfp4: bf16 or fp32 weights, got {w.dtype}")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    if q is None:
+        q = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.uint8, device=w.device)
+    _check(_lib.lib().moe_quantize_mxfp4(rows, K, dt, _ptr(w, None, "w"), _ptr(q, torch.uint8, "q"),
+                                         _ptr(scales, torch.uint8, "scales"), _stream(stream)),
+           "moe_quantize_mxfp4")
+    return q, scales
+
+
+def expert_ffn_mxfp4(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None):
+    """moe_expert_ffn_mxfp4; w1, w3, w2 are (codes, scales) pairs from quantize_mxfp4."""
+    c = d.c()
+    dt = d.torch_dtype
+    (q1, s1), (q3, s3), (q2, s2) = w1, w3, w2
+    u8 = torch.uint8
+    _check(_lib.lib().moe_expert_ffn_mxfp4(
+        C.byref(c), _ptr(x_packed, dt, "x_packed"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(q1, u8, "w1q"), _ptr(s1, u8, "w1s"), _ptr(q3, u8, "w3q"), _ptr(s3, u8, "w3s"),
+        _ptr(q2, u8, "w2q"), _ptr(s2, u8, "w2s"), _ptr(y_packed, dt, "y_packed"),
+        _ptr(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)),
+        "moe_expert_ffn_mxfp4")
+
+
+def layer_forward_mxfp4(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None,
+                        debug=None, stream=None):
+    """The fused layer with MXFP4 expert weights ((codes, scales) pairs from quantize_mxfp4,
+    the shared expert's in `shared`).  Returns y."""
+    dt = d.torch_dtype
+    if y is None:
+        y = torch.empty((d.T, d.H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(d, x.device)
+    u8 = torch.uint8
+    none = (None, None)
+    (q1, s1), (q3, s3), (q2, s2) = w1, w3, w2
+    (e1, t1), (e3, t3), (e2, t2) = shared if shared is not None else (none, none, none)
+    dbg = _debug_struct(debug) if debug else None
+    c = d.c()
+    _check(_lib.lib().moe_layer_forward_mxfp4(
+        C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),
+        _ptr(q1, u8, "w1q"), _ptr(s1, u8, "w1s"), _ptr(q3, u8, "w3q"), _ptr(s3, u8, "w3s"),
+        _ptr(q2, u8, "w2q"), _ptr(s2, u8, "w2s"), _ptr(e1, u8, "ws1q"), _ptr(t1, u8, "ws1s"),
+        _ptr(e3, u8, "ws3q"), _ptr(t3, u8, "ws3s"), _ptr(e2, u8, "ws2q"), _ptr(t2, u8, "ws2s"),
+        _ptr(y, dt, "y"), C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"),
+        ws.numel(), _stream(stream)), "moe_layer_forward_mxfp4")
+    return y
+
+
 def expert_ffn_fp8(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None):
     """moe_expert_ffn_fp8; w1, w3, w2 are (codes, scales) pairs from quantize_fp8."""
     c = d.c()

@@ -185,10 +185,29 @@ PermuteArgs permute_args(const moe_dims_t* d, const Layout& L, void* ws) {
 // fp32 scale per row (bf16 layers only)
 struct ExpertWeights {
   const void *w1, *w3, *w2;
-  const float *s1, *s3, *s2;
+  const float *s1, *s3, *s2;      // FP8 E4M3: per-row scales
+  const uint8_t *m1, *m3, *m2;    // MXFP4: E8M0 scales per 32 k
   bool fp8() const { return s1 != nullptr; }
-  bool complete() const { return w1 && w3 && w2 && (!s1 || (s3 && s2)) && (s1 || (!s3 && !s2)); }
+  bool mx() const { return m1 != nullptr; }
+  int fmt() const { return fp8() ? 1 : mx() ? 2 : 0; }
+  bool complete() const {
+    const bool s = s1 && s3 && s2, no_s = !s1 && !s3 && !s2;
+    const bool m = m1 && m3 && m2, no_m = !m1 && !m3 && !m2;
+    return w1 && w3 && w2 && (s || no_s) && (m || no_m) && !(s && m);
+  }
 };
+
+ExpertWeights plain_weights(const void* w1, const void* w3, const void* w2) {
+  return ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+}
+ExpertWeights fp8_weights(const void* w1, const float* s1, const void* w3, const float* s3,
+                          const void* w2, const float* s2) {
+  return ExpertWeights{w1, w3, w2, s1, s3, s2, nullptr, nullptr, nullptr};
+}
+ExpertWeights mxfp4_weights(const void* w1, const uint8_t* s1, const void* w3, const uint8_t* s3,
+                            const void* w2, const uint8_t* s2) {
+  return ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr, s1, s3, s2};
+}
 
 // grouped gate-up + down over G groups whose packed row ranges are offsets[0..G]; groups past
 // G_routed (at most one) take the extra weights X
@@ -199,8 +218,9 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
                    void* const* ev = nullptr, const int32_t* group_slot = nullptr) {
   const bool bf16 = d->dtype == MOE_BF16;
   // groups past G_routed take the extra weights; there must be some for them, stored like W's
-  if (G_routed < 0 || G_routed > G || !W.complete() || (W.fp8() && !bf16)) return hipErrorInvalidValue;
-  if (G > G_routed && (!X || !X->complete() || X->fp8() != W.fp8())) return hipErrorInvalidValue;
+  if (G_routed < 0 || G_routed > G || !W.complete() || (W.fmt() && !bf16)) return hipErrorInvalidValue;
+  if (G > G_routed && (!X || !X->complete() || X->fmt() != W.fmt())) return hipErrorInvalidValue;
+  if (W.mx()) avg_rows = 0;  // MXFP4 runs on the 32-row tiles for every group size
   if (group_slot && !bf16) return hipErrorInvalidValue;  // slot indirection: MFMA path only
   int bm_gu, nt_gu, bm_dn, nt_dn;
   if (bf16) {
@@ -223,12 +243,16 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   gu.b2 = W.w3;
   gu.b_scale = W.s1;
   gu.b2_scale = W.s3;
+  gu.b_mx = W.m1;
+  gu.b2_mx = W.m3;
   gu.b_stride = (int64_t)I * d->H;
   if (G > G_routed) {
     gu.b_extra = X->w1;
     gu.b2_extra = X->w3;
     gu.b_scale_extra = X->s1;
     gu.b2_scale_extra = X->s3;
+    gu.b_mx_extra = X->m1;
+    gu.b2_mx_extra = X->m3;
   }
   gu.N = I;
   gu.K = d->H;
@@ -247,10 +271,12 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   dn.max_rows = max_rows;
   dn.b = W.w2;
   dn.b_scale = W.s2;
+  dn.b_mx = W.m2;
   dn.b_stride = (int64_t)d->H * I;
   if (G > G_routed) {
     dn.b_extra = X->w2;
     dn.b_scale_extra = X->s2;
+    dn.b_mx_extra = X->m2;
   }
   dn.N = d->H;
   dn.K = I;
@@ -396,7 +422,8 @@ moe_status_t expert_ffn_impl(const moe_dims_t* d, const void* x_packed, const in
   moe_status_t st = check_dims(d);
   if (st != MOE_OK) return st;
   if (!offsets || !W.complete()) return MOE_ERR_INVALID_ARG;
-  if (W.fp8() && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (W.fmt() && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (W.mx() && (d->H % 128 || d->I % 128)) return MOE_ERR_UNSUPPORTED;
   if (d->T > 0 && (!x_packed || !y_packed)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(d);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -416,8 +443,10 @@ extern "C" {
 moe_status_t moe_expert_ffn(const moe_dims_t* d, const void* x_packed, const int32_t* offsets,
                             const void* w1, const void* w3, const void* w2, void* y_packed,
                             void* ws, size_t ws_bytes, void* stream) {
-  return expert_ffn_impl(d, x_packed, offsets, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr},
-                         y_packed, ws, ws_bytes, stream);
+  return expert_ffn_impl(
+      d, x_packed, offsets,
+      plain_weights(w1, w3, w2), y_packed,
+      ws, ws_bytes, stream);
 }
 
 moe_status_t moe_expert_ffn_fp8(const moe_dims_t* d, const void* x_packed,
@@ -426,7 +455,29 @@ moe_status_t moe_expert_ffn_fp8(const moe_dims_t* d, const void* x_packed,
                                 const float* w2s, void* y_packed, void* ws, size_t ws_bytes,
                                 void* stream) {
   if (!w1s || !w3s || !w2s) return MOE_ERR_INVALID_ARG;
-  return expert_ffn_impl(d, x_packed, offsets, ExpertWeights{w1q, w3q, w2q, w1s, w3s, w2s},
+  return expert_ffn_impl(d, x_packed, offsets,
+                         fp8_weights(w1q, w1s, w3q, w3s, w2q, w2s),
+                         y_packed, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_quantize_mxfp4(int64_t rows, int32_t K, int32_t dtype, const void* w,
+                                uint8_t* q, uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || (dtype != MOE_BF16 && dtype != MOE_F32)) return MOE_ERR_INVALID_ARG;
+  if (K % 32) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_quantize_mxfp4(w, dtype == MOE_BF16, rows, K, q, scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_mxfp4(const moe_dims_t* d, const void* x_packed,
+                                  const int32_t* offsets, const uint8_t* w1q, const uint8_t* w1s,
+                                  const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                  const uint8_t* w2s, void* y_packed, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (!w1s || !w3s || !w2s) return MOE_ERR_INVALID_ARG;
+  return expert_ffn_impl(d, x_packed, offsets,
+                         mxfp4_weights(w1q, w1s, w3q, w3s, w2q, w2s),
                          y_packed, ws, ws_bytes, stream);
 }
 
@@ -475,14 +526,15 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
     if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     const CacheView v = cache_view(cu->cache);
     if (v.E != d->E || v.H != d->H || v.I != d->I) return MOE_ERR_INVALID_ARG;
-    W = ExpertWeights{v.w1, v.w3, v.w2, nullptr, nullptr, nullptr};
+    W = plain_weights(v.w1, v.w3, v.w2);
     group_slot = v.table;
   }
   if (!x || !wg || !W.complete() || !y) {
     if (d->T > 0) return MOE_ERR_INVALID_ARG;
   }
-  if (W.fp8() && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (d->I_shared > 0 && (!SW.complete() || SW.fp8() != W.fp8())) return MOE_ERR_INVALID_ARG;
+  if (W.fmt() && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (W.mx() && (d->H % 128 || d->I % 128 || d->I_shared % 128)) return MOE_ERR_UNSUPPORTED;
+  if (d->I_shared > 0 && (!SW.complete() || SW.fmt() != W.fmt())) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(d);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
@@ -583,8 +635,8 @@ moe_status_t moe_layer_forward(const moe_dims_t* d, const void* x, const void* w
                                const void* ws1, const void* ws3, const void* ws2, void* y,
                                const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
                                void* stream) {
-  return layer_forward_impl(d, x, wg, bias, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr},
-                            ExpertWeights{ws1, ws3, ws2, nullptr, nullptr, nullptr}, y, dbg, ws,
+  return layer_forward_impl(d, x, wg, bias, plain_weights(w1, w3, w2),
+                            plain_weights(ws1, ws3, ws2), y, dbg, ws,
                             ws_bytes, stream);
 }
 
@@ -597,8 +649,24 @@ moe_status_t moe_layer_forward_cached(const moe_dims_t* d, const void* x, const 
   if (info) *info = moe_cache_step_t{};
   const CacheUse cu{cache, (hipStream_t)copy_stream, info};
   return layer_forward_impl(d, x, wg, bias, ExpertWeights{},
-                            ExpertWeights{ws1, ws3, ws2, nullptr, nullptr, nullptr}, y, dbg, ws,
+                            plain_weights(ws1, ws3, ws2), y, dbg, ws,
                             ws_bytes, stream, &cu);
+}
+
+moe_status_t moe_layer_forward_mxfp4(const moe_dims_t* d, const void* x, const void* wg,
+                                     const float* bias, const uint8_t* w1q, const uint8_t* w1s,
+                                     const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                     const uint8_t* w2s, const uint8_t* ws1q, const uint8_t* ws1s,
+                                     const uint8_t* ws3q, const uint8_t* ws3s,
+                                     const uint8_t* ws2q, const uint8_t* ws2s, void* y,
+                                     const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (d && d->T > 0 && (!w1s || !w3s || !w2s)) return MOE_ERR_INVALID_ARG;
+  if (d && d->I_shared > 0 && (!ws1s || !ws3s || !ws2s)) return MOE_ERR_INVALID_ARG;
+  return layer_forward_impl(
+      d, x, wg, bias, mxfp4_weights(w1q, w1s, w3q, w3s, w2q, w2s),
+      mxfp4_weights(ws1q, ws1s, ws3q, ws3s, ws2q, ws2s), y, dbg, ws,
+      ws_bytes, stream);
 }
 
 moe_status_t moe_layer_forward_fp8(const moe_dims_t* d, const void* x, const void* wg,
@@ -610,9 +678,10 @@ moe_status_t moe_layer_forward_fp8(const moe_dims_t* d, const void* x, const voi
                                    void* ws, size_t ws_bytes, void* stream) {
   if (d && d->T > 0 && (!w1s || !w3s || !w2s)) return MOE_ERR_INVALID_ARG;
   if (d && d->I_shared > 0 && (!ws1s || !ws3s || !ws2s)) return MOE_ERR_INVALID_ARG;
-  return layer_forward_impl(d, x, wg, bias, ExpertWeights{w1q, w3q, w2q, w1s, w3s, w2s},
-                            ExpertWeights{ws1q, ws3q, ws2q, ws1s, ws3s, ws2s}, y, dbg, ws,
-                            ws_bytes, stream);
+  return layer_forward_impl(
+      d, x, wg, bias, fp8_weights(w1q, w1s, w3q, w3s, w2q, w2s),
+      fp8_weights(ws1q, ws1s, ws3q, ws3s, ws2q, ws2s), y, dbg, ws,
+      ws_bytes, stream);
 }
 
 }  // extern "C"

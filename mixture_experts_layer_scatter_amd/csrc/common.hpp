@@ -98,6 +98,13 @@ struct GroupedGemm {
   const float* b2_scale;
   const float* b_scale_extra;
   const float* b2_scale_extra;
+  // MXFP4 weights (two E2M1 codes per byte, element 2j in the low nibble; bf16 MFMA path only):
+  // E8M0 scales [N, K/32] per group, b_mx + w * N * (K/32) (b2_mx for b2, *_mx_extra for the
+  // extra group).  Null b_mx: no MXFP4.
+  const uint8_t* b_mx;
+  const uint8_t* b2_mx;
+  const uint8_t* b_mx_extra;
+  const uint8_t* b2_mx_extra;
   // [G_routed] or null: routed group g's weights are matrix group_slot[g] of b / b2 (an expert
   // cache's slot); null: matrix g (bf16 MFMA path only)
   const int32_t* group_slot;
@@ -143,6 +150,9 @@ CacheView cache_view(const moe_expert_cache* c);
 // quant.hip: per-row FP8 E4M3 quantisation of a [rows, K] bf16 or fp32 matrix (K % 8 == 0)
 hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
                                float* scales, hipStream_t s);
+// MXFP4 quantisation (K % 32 == 0): codes [rows, K/2], E8M0 scales [rows, K/32]
+hipError_t launch_quantize_mxfp4(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
+                                 uint8_t* scales, hipStream_t s);
 
 // out[i] = sum_s part[s * n + i] (fixed order)
 hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* out, hipStream_t s);

@@ -48,7 +48,11 @@
 //    applies silu(a) * g before one bf16 store of the activation.
 //  * The gate (fp32 logits) can split its reduction over ksplit workgroups per
 //    tile; the partial sums are added in a fixed order afterwards.
-//  * FP8 weights (WQ): the weight tile travels HBM -> LDS as E4M3 bytes (half
+//  * MXFP4 weights (WQ = 2): E2M1 codes, two per byte, with an E8M0 scale per
+//    32 k of a row; the code tile and the scale tile both travel into LDS, and
+//    a fragment read widens 8 codes with the hardware's scaled conversion (the
+//    products are exact in bf16), so the scales never reach the epilogue.
+//  * FP8 weights (WQ = 1): the weight tile travels HBM -> LDS as E4M3 bytes (half
 //    the bytes of bf16, the point for the weight-streaming decode shape); a
 //    fragment read takes 8 codes and widens them to bf16 in registers (every
 //    E4M3 value is exact in bf16), so the same bf16 MFMA runs; the per-row scale
@@ -69,6 +73,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
                                            int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+// the same with 4 bytes per lane (256 bytes per wavefront)
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                          int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
@@ -132,6 +141,20 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 v) {
   return r.h;
 }
 
+// eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times a power-of-two
+// scale -> eight bf16 values (exact: E2M1 values have two significant bits)
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
+  union {
+    uint32_t u[4];
+    bf16x8 h;
+  } r;
+  r.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  r.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  r.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  r.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  return r.h;
+}
+
 template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_ = 64>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
@@ -149,15 +172,24 @@ struct TileShape {
   static_assert(A_LOADS * RPL * WAVES == BM, "load split");
 };
 
-// LDS geometry of a shape with bf16 (WQ = false) or E4M3 (WQ = true) weights
-template <class SH, bool WQ>
+// weight storage of the grouped GEMM's second operand
+constexpr int kWBf16 = 0, kWFp8 = 1, kWMxfp4 = 2;
+
+// LDS geometry of a shape with bf16, E4M3 or MXFP4 weights
+template <class SH, int WQ>
 struct Geo {
-  static constexpr int B_ROWB = WQ ? SH::BK : SH::ROWB;  // bytes of one weight row of a stage
+  static constexpr int B_ROWB = WQ == kWBf16 ? SH::ROWB : WQ == kWFp8 ? SH::BK : SH::BK / 2;
   static constexpr int B_CH = B_ROWB / 16;            // its 16-byte chunks
   static constexpr int B_RPL = 1024 / B_ROWB;         // weight rows one 1 KB load covers
   static constexpr int B_LOADS = SH::BN / B_RPL / SH::WAVES;
-  static constexpr int L = SH::A_LOADS + B_LOADS;     // loads per wavefront per stage
-  static constexpr int STAGE = SH::A_BYTES + SH::BN * B_ROWB;
+  // MXFP4: the stage's E8M0 scales, one dword (BK / 32 = 4 blocks) per weight row, loaded 32
+  // rows per wavefront load into 256-byte areas (the other 32 lanes carry no address)
+  static constexpr int SC_LOADS = WQ == kWMxfp4 ? SH::BN / 32 / SH::WAVES : 0;
+  static constexpr int SC_BYTES = WQ == kWMxfp4 ? SH::BN / 32 * 256 : 0;
+  static constexpr int L = SH::A_LOADS + B_LOADS + SC_LOADS;  // loads per wavefront per stage
+  static constexpr int STAGE = SH::A_BYTES + SH::BN * B_ROWB + SC_BYTES;
+  static_assert(WQ != kWMxfp4 || (SH::BK == 128 && SC_LOADS * 32 * SH::WAVES == SH::BN),
+                "MXFP4 stages hold 128 k: one scale dword per row");
   static constexpr int LDS = SH::S * STAGE;
   static_assert(B_LOADS * B_RPL * SH::WAVES == SH::BN, "load split");
   static_assert(SH::S >= 2 && (SH::S - 2) * L < 64, "stages in flight fit the vmcnt counter");
@@ -175,6 +207,9 @@ using DecodeShape = TileShape<32, 256, 1, 4, 4>;
 using PrefillShapeFp8 = TileShape<256, 256, 2, 4, 2>;
 using DecodeShapeFp8 = TileShape<32, 256, 1, 4, 3>;
 using DecodeShapeFp8K128 = TileShape<32, 256, 1, 4, 2, 128>;
+// MXFP4: 128-k stages (64-byte code rows, one scale dword per row), three of them (78 KB) so
+// that two workgroups fit per CU; every group size runs on this 32-row shape
+using ShapeMxfp4 = TileShape<32, 256, 1, 4, 3, 128>;
 
 // ---- tile bookkeeping shared by the GEMM and its tail reduction ---------------------------------
 
@@ -239,7 +274,7 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int xcd, int nx, int kt
 // The epilogue: lane holds token l32 of block i and columns 8q + 4hi + (0..3) of each
 // 32-column block j (the weights were the MFMA's first operand: D[column][token]).  With FP8
 // weights each column's accumulator is first multiplied by its weight row's scale.
-template <class SH, int EPI, bool WQ>
+template <class SH, int EPI, int WQ>
 __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& t, int ks,
                                            const f32x16 (&acc)[SH::TM][SH::TN], int wm, int wn,
                                            int l32, int hi, int i_only = -1) {
@@ -247,7 +282,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
   const int64_t out_row0 = (int64_t)t.row_base + t.m0;
   // per-column scales of this tile (1 for bf16 weights), loaded once for all token blocks
   float4 sc[TN][4];
-  if constexpr (WQ) {
+  if constexpr (WQ == kWFp8) {
     const bool extra = p.tile_start && t.g >= p.G_routed;
     const float* s1 = extra ? p.b_scale_extra : p.b_scale + (int64_t)t.w * p.N;
     const float* s2 = EPI != EPI_SWIGLU ? s1
@@ -265,7 +300,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
       }
   }
   auto scaled = [&](int i, int j, int q, int e) -> float {
-    if constexpr (WQ) {
+    if constexpr (WQ == kWFp8) {
       const float4 v = sc[j][q];
       const float f = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
       return acc[i][j][4 * q + e] * f;
@@ -338,14 +373,15 @@ __device__ __forceinline__ float4* tail_slot(const GroupedGemm& p, int xcd, int 
   return (float4*)(p.tail_part + ((int64_t)xcd * kTailPieces + slot) * kRegs * SH::THREADS);
 }
 
-template <class SH, int EPI, bool GATHER, int GN, bool WQ>
+template <class SH, int EPI, bool GATHER, int GN, int WQ>
 __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   using GE = Geo<SH, WQ>;
   constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, L = GE::L;
   constexpr int TM = SH::TM, TN = SH::TN, KK = SH::KK, RPL = SH::RPL;
   constexpr int B_ROWB = GE::B_ROWB, B_RPL = GE::B_RPL, B_LOADS = GE::B_LOADS, B_CH = GE::B_CH;
   constexpr int ROWB = SH::ROWB, CH = SH::CH;
-  constexpr int STAGE = GE::STAGE, WB = WQ ? 1 : 2;  // weight bytes per element
+  constexpr int STAGE = GE::STAGE, SC_LOADS = GE::SC_LOADS;
+  constexpr int SC_OFF = SH::A_BYTES + SH::BN * GE::B_ROWB;  // scale tile in a stage
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs W1 and W3 blocks");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -396,7 +432,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 
   // per-lane source offsets of the current tile's loads (lane: row lane / 8, chunk lane % 8)
   uint32_t a_off[SH::A_LOADS], b_off[B_LOADS];
-  __amdgpu_buffer_rsrc_t rB, rB2;
+  uint32_t s_off[SC_LOADS > 0 ? SC_LOADS : 1];
+  __amdgpu_buffer_rsrc_t rB, rB2, rS, rS2;
   int kt0 = 0, ktn = 0;
   auto setup = [&](const Tile& t) {
     // uniform, but the 64-bit divisions that split k leave them in VGPRs; a VGPR soffset would
@@ -405,14 +442,31 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     ktn = __builtin_amdgcn_readfirstlane(t.ktn);
     const bool extra = p.tile_start && t.loc.g >= p.G_routed;
     const int wsel = __builtin_amdgcn_readfirstlane(t.loc.w);  // uniform: keeps the rsrc scalar
+    // bytes of one weight row and of one group's matrix
+    const int64_t wrow = WQ == kWBf16 ? 2LL * K : WQ == kWFp8 ? (int64_t)K : (int64_t)K / 2;
+    const int64_t gbytes = WQ == kWBf16 ? p.b_stride * 2 : WQ == kWFp8 ? p.b_stride : p.b_stride / 2;
     const char* bbase =
-        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)wsel * p.b_stride * WB);
+        (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)wsel * gbytes);
     const char* b2base = bbase;
     if (EPI == EPI_SWIGLU)
-      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)wsel * p.b_stride * WB);
-    const uint32_t b_bytes = (uint32_t)((int64_t)p.N * K * WB);
+      b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)wsel * gbytes);
+    const uint32_t b_bytes = (uint32_t)((int64_t)p.N * wrow);
     rB = make_rsrc(bbase, b_bytes);
     rB2 = make_rsrc(b2base, b_bytes);
+    if constexpr (WQ == kWMxfp4) {
+      const int64_t srow = K / 32, sgroup = (int64_t)p.N * srow;
+      const uint8_t* sbase = extra ? p.b_mx_extra : p.b_mx + (int64_t)wsel * sgroup;
+      const uint8_t* s2base = sbase;
+      if (EPI == EPI_SWIGLU) s2base = extra ? p.b2_mx_extra : p.b2_mx + (int64_t)wsel * sgroup;
+      rS = make_rsrc(sbase, (uint32_t)sgroup);
+      rS2 = make_rsrc(s2base, (uint32_t)sgroup);
+#pragma unroll
+      for (int i = 0; i < SC_LOADS; ++i) {
+        const int n = (wid * SC_LOADS + i) * 32 + lane;  // lanes 32..63 load nothing
+        const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
+        s_off[i] = lane < 32 && src < p.N ? (uint32_t)(src * srow) : kOutOfRange;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i) {
       const int r = (wid * SH::A_LOADS + i) * RPL + lane / CH;
@@ -431,7 +485,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       const int n = (wid * B_LOADS + i) * B_RPL + lane / B_CH;
       const int c = (lane % B_CH) ^ row_swizzle<B_CH>(n);
       const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
-      b_off[i] = src < p.N ? (uint32_t)src * (uint32_t)K * WB + c * 16 : kOutOfRange;
+      b_off[i] = src < p.N ? (uint32_t)(src * wrow) + c * 16 : kOutOfRange;
     }
   };
   // local k-step lk of the current tile into LDS slot `slot`; lk >= ktn loads nothing
@@ -450,6 +504,16 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       const bool second = EPI == EPI_SWIGLU && (((blk * B_RPL) >> 5) & 1);
       load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kbw);
     }
+    if constexpr (WQ == kWMxfp4) {
+      // the stage's 4 scale bytes of each row (k-blocks (kt0 + lk) * 4 .. + 3)
+      const int kbs = valid ? (kt0 + lk) * 4 : 0;
+#pragma unroll
+      for (int i = 0; i < SC_LOADS; ++i) {
+        const int blk = wid * SC_LOADS + i;
+        const bool second = EPI == EPI_SWIGLU && (blk & 1);
+        load_lds4(second ? rS2 : rS, sa + SC_OFF + blk * 256, valid ? s_off[i] : kOutOfRange, kbs);
+      }
+    }
   };
   auto prologue = [&]() {
 #pragma unroll
@@ -462,7 +526,19 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 32 * ROWB);
-    if constexpr (WQ) {
+    if constexpr (WQ == kWMxfp4) {
+      // a k-sub's 16 codes are half of chunk kk / 2 of the 64-byte row; the lane takes 8 of them
+      // (one dword) and the scale of their 32-block kk / 2
+      const uint32_t woff = (uint32_t)((((kk >> 1) ^ swb) * 16) + (kk & 1) * 8 + hi * 4);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t codes = *(const uint32_t*)(st + b_frag + woff + j * 32 * B_ROWB);
+        const uint32_t sc4 =
+            *(const uint32_t*)(st + SC_OFF + ((wn * SH::WTN) / 32 + j) * 256 + l32 * 4);
+        const float scale = __uint_as_float(((sc4 >> (8 * (kk >> 1))) & 0xffu) << 23);
+        fb[buf][j] = fp4x8_to_bf16(codes, scale);
+      }
+    } else if constexpr (WQ == kWFp8) {
       // a k-sub's 16 codes are chunk kk of the row; the lane takes half of it
       const uint32_t woff = (uint32_t)(((kk ^ swb) * 16) + hi * 8);
 #pragma unroll
@@ -562,7 +638,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 
 // The split tail tiles: add each tile's fp32 partials in piece order, then the epilogue.  One
 // workgroup per (XCD, tail tile, token block i), so the reduction spreads over many CUs.
-template <class SH, int EPI, int GN, bool WQ>
+template <class SH, int EPI, int GN, int WQ>
 __global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, int nx) {
   constexpr int TM = SH::TM, TN = SH::TN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -600,7 +676,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, i
   store_tile<SH, EPI, WQ>(p, loc, 0, acc, wm, wn, lane & 31, lane >> 5, ib);
 }
 
-template <class SH, int EPI, bool GATHER, int GN, bool WQ = false>
+template <class SH, int EPI, bool GATHER, int GN, int WQ = kWBf16>
 static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStream_t s) {
   constexpr int LDS = Geo<SH, WQ>::LDS;
   auto kern = gemm_kernel<SH, EPI, GATHER, GN, WQ>;
@@ -668,23 +744,33 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   }
   const bool big = bm == PrefillShape::BM;
   const bool gather = p.row_map != nullptr;
+  if (p.b_mx) {  // MXFP4 weights: the 32-row shape for every group size, K % 128 == 0
+    if (p.K % 128 || (kind == GEMM_GATE_UP && !p.b2_mx)) return hipErrorInvalidValue;
+    if (p.G > p.G_routed && (!p.b_mx_extra || (kind == GEMM_GATE_UP && !p.b2_mx_extra)))
+      return hipErrorInvalidValue;
+    if (bm != ShapeMxfp4::BM) return hipErrorInvalidValue;  // tile map built for 32-row tiles
+    if (kind == GEMM_GATE_UP)
+      return gather ? run<ShapeMxfp4, EPI_SWIGLU, true, 1, kWMxfp4>(p, mt, num_cus, s)
+                    : run<ShapeMxfp4, EPI_SWIGLU, false, 1, kWMxfp4>(p, mt, num_cus, s);
+    return run<ShapeMxfp4, EPI_BF16, false, 1, kWMxfp4>(p, mt, num_cus, s);
+  }
   if (p.b_scale) {  // FP8 weights
     if (kind == GEMM_GATE_UP && !p.b2_scale) return hipErrorInvalidValue;
     if (p.G > p.G_routed && (!p.b_scale_extra || (kind == GEMM_GATE_UP && !p.b2_scale_extra)))
       return hipErrorInvalidValue;
     if (kind == GEMM_GATE_UP) {
       if (big)
-        return gather ? run<PrefillShapeFp8, EPI_SWIGLU, true, 8, true>(p, mt, num_cus, s)
-                      : run<PrefillShapeFp8, EPI_SWIGLU, false, 8, true>(p, mt, num_cus, s);
+        return gather ? run<PrefillShapeFp8, EPI_SWIGLU, true, 8, kWFp8>(p, mt, num_cus, s)
+                      : run<PrefillShapeFp8, EPI_SWIGLU, false, 8, kWFp8>(p, mt, num_cus, s);
       if (p.K % 128 == 0)
-        return gather ? run<DecodeShapeFp8K128, EPI_SWIGLU, true, 1, true>(p, mt, num_cus, s)
-                      : run<DecodeShapeFp8K128, EPI_SWIGLU, false, 1, true>(p, mt, num_cus, s);
-      return gather ? run<DecodeShapeFp8, EPI_SWIGLU, true, 1, true>(p, mt, num_cus, s)
-                    : run<DecodeShapeFp8, EPI_SWIGLU, false, 1, true>(p, mt, num_cus, s);
+        return gather ? run<DecodeShapeFp8K128, EPI_SWIGLU, true, 1, kWFp8>(p, mt, num_cus, s)
+                      : run<DecodeShapeFp8K128, EPI_SWIGLU, false, 1, kWFp8>(p, mt, num_cus, s);
+      return gather ? run<DecodeShapeFp8, EPI_SWIGLU, true, 1, kWFp8>(p, mt, num_cus, s)
+                    : run<DecodeShapeFp8, EPI_SWIGLU, false, 1, kWFp8>(p, mt, num_cus, s);
     }
-    if (big) return run<PrefillShapeFp8, EPI_BF16, false, 8, true>(p, mt, num_cus, s);
-    if (p.K % 128 == 0) return run<DecodeShapeFp8K128, EPI_BF16, false, 1, true>(p, mt, num_cus, s);
-    return run<DecodeShapeFp8, EPI_BF16, false, 1, true>(p, mt, num_cus, s);
+    if (big) return run<PrefillShapeFp8, EPI_BF16, false, 8, kWFp8>(p, mt, num_cus, s);
+    if (p.K % 128 == 0) return run<DecodeShapeFp8K128, EPI_BF16, false, 1, kWFp8>(p, mt, num_cus, s);
+    return run<DecodeShapeFp8, EPI_BF16, false, 1, kWFp8>(p, mt, num_cus, s);
   }
   if (kind == GEMM_GATE_UP) {
     if (big)

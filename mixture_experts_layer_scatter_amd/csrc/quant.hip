@@ -80,6 +80,81 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* __restric
   }
 }
 
+// MXFP4 (the OCP microscaling format's E2M1 elements, one E8M0 scale per 32 consecutive k):
+// per block, shared = clamp(floor(log2(amax)) - 2, -126, 127) (2 = the largest E2M1 exponent),
+// scale code shared + 127 (127 for a zero block), and each element the E2M1 code nearest to
+// w / 2^shared, ties to even, saturating at +-6 (the hardware's scaled conversion, which
+// divides by the scale).  One thread per block of 32; codes two per byte, low nibble first.
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const void* __restrict__ w,
+                                                             int64_t blocks,
+                                                             uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ scales) {
+  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < blocks;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    float v[32];
+    if constexpr (BF16) {
+      const uint4* src = (const uint4*)((const uint16_t*)w + b * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = src[i];
+        const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = __uint_as_float(h[j] << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float(h[j] & 0xffff0000u);
+        }
+      }
+    } else {
+      const float4* src = (const float4*)((const float*)w + b * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 f = src[i];
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    uint8_t code = 127;
+    if (amax > 0.f) {
+      // amax = m * 2^e with m in [0.5, 1): floor(log2(amax)) = e - 1
+      int shared = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;
+      shared = shared < -126 ? -126 : (shared > 127 ? 127 : shared);
+      code = (uint8_t)(shared + 127);
+      const float scale = __uint_as_float((uint32_t)code << 23);  // 2^shared, a normal float
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t r = 0;
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 0], v[8 * d + 1], scale, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 2], v[8 * d + 3], scale, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 4], v[8 * d + 5], scale, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 6], v[8 * d + 7], scale, 3);
+        packed[d] = r;
+      }
+    }
+    *(uint4*)(q + b * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    scales[b] = code;
+  }
+}
+
+hipError_t launch_quantize_mxfp4(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
+                                 uint8_t* scales, hipStream_t s) {
+  const int64_t blocks = rows * (K / 32);
+  if (blocks <= 0) return hipSuccess;
+  const int64_t g = (blocks + 255) / 256;
+  const int grid = g < 65536 ? (int)g : 65536;
+  if (bf16)
+    quantize_mxfp4_kernel<true><<<grid, 256, 0, s>>>(w, blocks, q, scales);
+  else
+    quantize_mxfp4_kernel<false><<<grid, 256, 0, s>>>(w, blocks, q, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
                                float* scales, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

@@ -205,3 +205,25 @@ def test_cache_argument_checks():
     lib.moe_cache_destroy(None)  # no-op
     assert lib.moe_layer_forward_cached(C.byref(d), p, p, None, None, None, None, None, p, None,
                                         p, 1 << 40, None, None, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_mxfp4_entry_point_checks():
+    L = _lib()
+    lib = L.lib()
+    p = C.c_void_p(16)  # never dereferenced
+    assert lib.moe_quantize_mxfp4(4, 48, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp4(4, 0, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(4, 64, 5, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(4, 64, L.MOE_BF16, p, None, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(0, 64, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    d = _dims()  # H = I = 128
+    assert lib.moe_expert_ffn_mxfp4(C.byref(d), p, p, p, None, p, p, p, p, p, p, 1 << 40,
+                                    None) == L.MOE_ERR_INVALID_ARG
+    # MXFP4 stages hold 128 k: H and I must be multiples of 128
+    d192 = _dims(I=192)
+    assert lib.moe_expert_ffn_mxfp4(C.byref(d192), p, p, p, p, p, p, p, p, p, p, 1 << 40,
+                                    None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_forward_mxfp4(C.byref(_dims(H=192)), *([p] * 16), None, p, 1 << 40,
+                                       None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_forward_mxfp4(C.byref(_dims(dtype=L.MOE_F32)), *([p] * 16), None, p,
+                                       1 << 40, None) == L.MOE_ERR_UNSUPPORTED
