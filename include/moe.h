@@ -238,18 +238,28 @@ moe_status_t moe_quantize_fp8(int64_t rows, int32_t K, int32_t dtype, const void
  * with bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0
  * scale 2^(s - 127) per 32 consecutive elements of a row, a reading of [P3]
  * §5.2's 4-bit expert weights (weight-only here; activations stay bf16).
- *  w [rows, K] of storage `dtype` (MOE_BF16 or MOE_F32), K % 32 == 0.
+ *  w [rows, K] of storage `dtype` (MOE_BF16 or MOE_F32), rows % 32 == 0 and
+ *  K % 128 == 0 (else MOE_ERR_UNSUPPORTED).
  *  Per block of 32: amax = max |w|; 0 gives scale code 127 and codes 0; else
  *  shared = clamp(floor(log2(amax)) - 2, -126, 127), scale code = shared + 127,
  *  and each code the E2M1 value nearest to w / 2^shared (ties to even,
  *  saturating at +-6).
- *  q [rows, K/2] u8: element 2j in the low nibble of byte j; scales
- *  [rows, K/32] u8.  Quantise w1 and w3 as [E*I, H] and w2 as [E*H, I]. */
+ *  Both outputs are blocked by 32 rows and 128 k, so that what the grouped
+ *  GEMM reads for 32 weight rows and 128 k is whole 128-byte lines:
+ *  q: rows * K/2 bytes, [rows/32, K/128, 32, 64]: element k of row r in byte
+ *  ((r/32) * (K/128) + k/128) * 2048 + (r%32) * 64 + (k%128)/2, the low
+ *  nibble for even k;
+ *  scales: rows * K/32 bytes, [rows/32, K/128, 32, 4]: the scale of row r,
+ *  block b (elements 32b .. 32b+31) at byte
+ *  ((r/32) * (K/128) + b/4) * 128 + (r%32) * 4 + b%4.
+ *  Quantise w1 and w3 as [E*I, H] and w2 as [E*H, I] (I % 32 == 0 keeps an
+ *  expert's codes and scales contiguous, E*I*H/2 and E*I*H/32 bytes). */
 moe_status_t moe_quantize_mxfp4(int64_t rows, int32_t K, int32_t dtype, const void* w,
                                 uint8_t* q, uint8_t* scales, void* stream);
 
-/* moe_expert_ffn with MXFP4 weights (codes and scales as moe_quantize_mxfp4
- * writes them; w1/w3 scales [E*I, H/32], w2 scales [E*H, I/32]).  dims->dtype
+/* moe_expert_ffn with MXFP4 weights (blocked codes and scales as
+ * moe_quantize_mxfp4 writes them for w1/w3 as [E*I, H] and w2 as [E*H, I]).
+ * dims->dtype
  * must be MOE_BF16, H and I multiples of 128.  The codes widen, times their
  * block scale, exactly to bf16 for the MFMA.  Every group size runs on the
  * 32-row tiles (the weight-streaming shape). */

@@ -175,17 +175,24 @@ def quantize_fp8(w, q=None, scales=None, stream=None):
 
 
 def quantize_mxfp4(w, q=None, scales=None, stream=None):
-    """MXFP4 quantisation of a bf16 or fp32 device tensor [..., K] (K % 32 == 0).  Returns (codes
-    uint8 [..., K/2], two per byte, low nibble first; E8M0 scales uint8 [..., K/32])."""
+    """MXFP4 quantisation of a bf16 or fp32 device tensor [..., R, K] (R % 32 == 0,
+    K % 128 == 0).  Returns (E2M1 codes uint8 [..., R/32, K/128, 32 * 64], two per byte, low
+    nibble first: [r/32, k/128, (r%32)*64 + (k%128)/2] holds element k of row r; E8M0 scales
+    uint8 [..., R/32, K/128, 32 * 4]: [r/32, b/4, (r%32)*4 + b%4] holds the scale of row r,
+    32-block b) -- both blocked by 32 rows and 128 k."""
     dt = {torch.bfloat16: _lib.MOE_BF16, torch.float32: _lib.MOE_F32}.get(w.dtype)
     if dt is None:
         raise TypeError(f"quantize_mxfp4: bf16 or fp32 weights, got {w.dtype}")
-    K = w.shape[-1]
+    if w.dim() < 2:
+        raise ValueError("quantize_mxfp4: weights [..., R, K]")
+    R, K = w.shape[-2], w.shape[-1]
     rows = w.numel() // K
     if q is None:
-        q = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+        q = torch.empty(w.shape[:-2] + (R // 32, K // 128, 2048), dtype=torch.uint8,
+                        device=w.device)
     if scales is None:
-        scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.uint8, device=w.device)
+        scales = torch.empty(w.shape[:-2] + (R // 32, K // 128, 128), dtype=torch.uint8,
+                             device=w.device)
     _check(_lib.lib().moe_quantize_mxfp4(rows, K, dt, _ptr(w, None, "w"), _ptr(q, torch.uint8, "q"),
                                          _ptr(scales, torch.uint8, "scales"), _stream(stream)),
            "moe_quantize_mxfp4")

@@ -463,7 +463,7 @@ moe_status_t moe_expert_ffn_fp8(const moe_dims_t* d, const void* x_packed,
 moe_status_t moe_quantize_mxfp4(int64_t rows, int32_t K, int32_t dtype, const void* w,
                                 uint8_t* q, uint8_t* scales, void* stream) {
   if (rows < 0 || K <= 0 || (dtype != MOE_BF16 && dtype != MOE_F32)) return MOE_ERR_INVALID_ARG;
-  if (K % 32) return MOE_ERR_UNSUPPORTED;
+  if (K % 128 || rows % 32) return MOE_ERR_UNSUPPORTED;  // the blocked scale layout
   if (rows == 0) return MOE_OK;
   if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;
   MOE_TRY(launch_quantize_mxfp4(w, dtype == MOE_BF16, rows, K, q, scales, (hipStream_t)stream));

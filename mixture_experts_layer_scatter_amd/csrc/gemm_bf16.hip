@@ -49,7 +49,9 @@
 //  * The gate (fp32 logits) can split its reduction over ksplit workgroups per
 //    tile; the partial sums are added in a fixed order afterwards.
 //  * MXFP4 weights (WQ = 2): E2M1 codes, two per byte, with an E8M0 scale per
-//    32 k of a row; the code tile and the scale tile both travel into LDS, and
+//    32 k of a row, both stored blocked by 32 rows and 128 k (one stage of a
+//    32-row block reads 2 KB of codes and one line of scales, all whole
+//    lines); the code and scale tiles travel into LDS, and
 //    a fragment read widens 8 codes with the hardware's scaled conversion (the
 //    products are exact in bf16), so the scales never reach the epilogue.
 //  * FP8 weights (WQ = 1): the weight tile travels HBM -> LDS as E4M3 bytes (half
@@ -454,7 +456,9 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     rB = make_rsrc(bbase, b_bytes);
     rB2 = make_rsrc(b2base, b_bytes);
     if constexpr (WQ == kWMxfp4) {
-      const int64_t srow = K / 32, sgroup = (int64_t)p.N * srow;
+      // scales blocked by 32 rows: the dword of row r for 128-k step kt at
+      // ((r / 32) * KT + kt) * 128 + (r % 32) * 4, so a block's 32 dwords are one line
+      const int64_t sgroup = (int64_t)p.N * (K / 32);
       const uint8_t* sbase = extra ? p.b_mx_extra : p.b_mx + (int64_t)wsel * sgroup;
       const uint8_t* s2base = sbase;
       if (EPI == EPI_SWIGLU) s2base = extra ? p.b2_mx_extra : p.b2_mx + (int64_t)wsel * sgroup;
@@ -464,7 +468,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       for (int i = 0; i < SC_LOADS; ++i) {
         const int n = (wid * SC_LOADS + i) * 32 + lane;  // lanes 32..63 load nothing
         const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
-        s_off[i] = lane < 32 && src < p.N ? (uint32_t)(src * srow) : kOutOfRange;
+        s_off[i] = lane < 32 && src < p.N ? (uint32_t)((src >> 5) * KT * 128 + (src & 31) * 4)
+                                          : kOutOfRange;
       }
     }
 #pragma unroll
@@ -485,7 +490,11 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       const int n = (wid * B_LOADS + i) * B_RPL + lane / B_CH;
       const int c = (lane % B_CH) ^ row_swizzle<B_CH>(n);
       const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
-      b_off[i] = src < p.N ? (uint32_t)(src * wrow) + c * 16 : kOutOfRange;
+      // MXFP4 codes are blocked: row r's 64 bytes of 128-k step kt at ((r / 32) * KT + kt) * 2048
+      // + (r % 32) * 64
+      const uint32_t row_at = WQ == kWMxfp4 ? (uint32_t)((src >> 5) * KT * 2048 + (src & 31) * 64)
+                                            : (uint32_t)(src * wrow);
+      b_off[i] = src < p.N ? row_at + c * 16 : kOutOfRange;
     }
   };
   // local k-step lk of the current tile into LDS slot `slot`; lk >= ktn loads nothing
@@ -494,7 +503,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     char* sa = smem + slot * STAGE;
     char* sb = sa + SH::A_BYTES;
     const int kb = valid ? (kt0 + lk) * ROWB : 0;
-    const int kbw = valid ? (kt0 + lk) * B_ROWB : 0;
+    const int kbw = valid ? (kt0 + lk) * (WQ == kWMxfp4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i)
       load_lds16(rA, sa + (wid * SH::A_LOADS + i) * 1024, valid ? a_off[i] : kOutOfRange, kb);
@@ -506,7 +515,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     }
     if constexpr (WQ == kWMxfp4) {
       // the stage's 4 scale bytes of each row (k-blocks (kt0 + lk) * 4 .. + 3)
-      const int kbs = valid ? (kt0 + lk) * 4 : 0;
+      const int kbs = valid ? (kt0 + lk) * 128 : 0;
 #pragma unroll
       for (int i = 0; i < SC_LOADS; ++i) {
         const int blk = wid * SC_LOADS + i;

@@ -85,11 +85,16 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* __restric
 // scale code shared + 127 (127 for a zero block), and each element the E2M1 code nearest to
 // w / 2^shared, ties to even, saturating at +-6 (the hardware's scaled conversion, which
 // divides by the scale).  One thread per block of 32; codes two per byte, low nibble first.
+// Both arrays are stored blocked by 32 rows and 128 k, the piece of a weight tile one stage of
+// the grouped GEMM reads: the 64 code bytes of a row's 128-k span follow those of the previous
+// row, so a 32-row block's span is 2 KB of whole lines; the four scales of a row's span sit in
+// one dword, and the dwords of 32 rows fill one 128-byte line.
 template <bool BF16>
 __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const void* __restrict__ w,
-                                                             int64_t blocks,
+                                                             int64_t blocks, int K,
                                                              uint8_t* __restrict__ q,
                                                              uint8_t* __restrict__ scales) {
+  const int nb = K / 32, spans = K / 128;
   for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < blocks;
        b += (int64_t)gridDim.x * blockDim.x) {
     float v[32];
@@ -137,8 +142,12 @@ __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const void* __restr
         packed[d] = r;
       }
     }
-    *(uint4*)(q + b * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    scales[b] = code;
+    const int64_t row = b / nb;
+    const int kb = (int)(b - row * nb);
+    const int64_t span = (row >> 5) * spans + (kb >> 2);
+    *(uint4*)(q + span * 2048 + (row & 31) * 64 + (kb & 3) * 16) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    scales[span * 128 + (row & 31) * 4 + (kb & 3)] = code;
   }
 }
 
@@ -149,9 +158,9 @@ hipError_t launch_quantize_mxfp4(const void* w, int bf16, int64_t rows, int K, u
   const int64_t g = (blocks + 255) / 256;
   const int grid = g < 65536 ? (int)g : 65536;
   if (bf16)
-    quantize_mxfp4_kernel<true><<<grid, 256, 0, s>>>(w, blocks, q, scales);
+    quantize_mxfp4_kernel<true><<<grid, 256, 0, s>>>(w, blocks, K, q, scales);
   else
-    quantize_mxfp4_kernel<false><<<grid, 256, 0, s>>>(w, blocks, q, scales);
+    quantize_mxfp4_kernel<false><<<grid, 256, 0, s>>>(w, blocks, K, q, scales);
   return hipGetLastError();
 }
 

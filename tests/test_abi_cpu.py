@@ -211,11 +211,14 @@ def test_mxfp4_entry_point_checks():
     L = _lib()
     lib = L.lib()
     p = C.c_void_p(16)  # never dereferenced
-    assert lib.moe_quantize_mxfp4(4, 48, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp4(32, 48, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
+    # the blocked scale layout takes rows in 32s and k in 128s
+    assert lib.moe_quantize_mxfp4(32, 96, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp4(48, 128, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_quantize_mxfp4(4, 0, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_quantize_mxfp4(4, 64, 5, p, p, p, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_quantize_mxfp4(4, 64, L.MOE_BF16, p, None, p, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_quantize_mxfp4(0, 64, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    assert lib.moe_quantize_mxfp4(32, 128, 5, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(32, 128, L.MOE_BF16, p, None, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
     d = _dims()  # H = I = 128
     assert lib.moe_expert_ffn_mxfp4(C.byref(d), p, p, p, None, p, p, p, p, p, p, 1 << 40,
                                     None) == L.MOE_ERR_INVALID_ARG

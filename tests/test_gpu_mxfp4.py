@@ -24,19 +24,31 @@ pytestmark = pytest.mark.gpu
 import mixture_experts_layer_scatter_amd as moe
 
 
+def unblock(a, rows, K, per_row):
+    """The library's codes or scales (blocked by 32 rows and 128 k: [rows/32, K/128, 32 rows,
+    per_row bytes]) as the row-major [rows, K/128 * per_row] array the oracle returns: a
+    re-indexing, no arithmetic."""
+    return (a.reshape(rows // 32, K // 128, 32, per_row).transpose(0, 2, 1, 3)
+            .reshape(rows, K // 128 * per_row))
+
+
 def _check_quant(src):
     q, s = moe.quantize_mxfp4(dev(src))
     torch.cuda.synchronize()
     oq, os_ = oracle.quantize_mxfp4(src)
-    assert np.array_equal(s.cpu().numpy(), os_), "scales differ"
-    gq = q.cpu().numpy()
-    bad = np.argwhere(gq != oq)
+    K = src.shape[-1]
+    rows = src.size // K
+    assert s.numel() == rows * K // 32 and q.numel() == rows * K // 2
+    assert np.array_equal(unblock(s.cpu().numpy(), rows, K, 4), os_.reshape(rows, K // 32)), \
+        "scales differ"
+    gq = unblock(q.cpu().numpy(), rows, K, 64)
+    bad = np.argwhere(gq != oq.reshape(rows, K // 2))
     assert len(bad) == 0, f"{len(bad)} code bytes differ, first {bad[:5].tolist()}"
     return q, s
 
 
-@pytest.mark.parametrize("rows,K,dtype", [(1, 32, "bf16"), (37, 128, "bf16"), (300, 7168, "bf16"),
-                                          (2048, 2048, "bf16"), (5, 4096, "f32"), (64, 96, "f32")])
+@pytest.mark.parametrize("rows,K,dtype", [(32, 128, "bf16"), (96, 384, "bf16"), (320, 7168, "bf16"),
+                                          (2048, 2048, "bf16"), (32, 4096, "f32"), (64, 256, "f32")])
 def test_quantize_bit_exact(rows, K, dtype):
     need_gpu()
     log(f"quantize mxfp4 rows={rows} K={K} {dtype}")
@@ -44,7 +56,7 @@ def test_quantize_bit_exact(rows, K, dtype):
     nb = K // 32
     w = (rng.standard_normal((rows, K)) * np.exp(rng.uniform(-12, 6, (rows, nb))).repeat(32, 1))
     w = w.astype(np.float32)
-    if rows > 3:
+    if rows > 3:  # every shape here
         w[1, :32] = 0.0                      # a zero block
         w[2, :32] = 0.0
         w[2, 5] = -3.0                       # one non-zero element
