@@ -59,6 +59,8 @@
 //    fragment read takes 8 codes and widens them to bf16 in registers (every
 //    E4M3 value is exact in bf16), so the same bf16 MFMA runs; the per-row scale
 //    multiplies the fp32 accumulator in the epilogue (it factors out of the sum).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -157,9 +159,14 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
   return r.h;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_ = 64>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_ = 64, int SB_ = S_>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  // LDS stages of the weight operand (S: of the token rows).  With 256 x 256 tiles two full
+  // stages take 128 KB of the 160 KB, so one operand can get a third slot: a step more of
+  // latency for its L2 misses
+  static constexpr int SB = SB_;
+  static_assert(SB == S || (S == 2 && SB == 3) || (S == 3 && SB == 2), "stage counts");
   static constexpr int BK = BK_;                      // k elements per LDS stage
   static constexpr int ROWB = BK * 2, CH = ROWB / 16; // bytes and 16-byte chunks of an A row
   static constexpr int WAVES = WM * WN, THREADS = WAVES * kWave;
@@ -188,17 +195,25 @@ struct Geo {
   // rows per wavefront load into 256-byte areas (the other 32 lanes carry no address)
   static constexpr int SC_LOADS = WQ == kWMxfp4 ? SH::BN / 32 / SH::WAVES : 0;
   static constexpr int SC_BYTES = WQ == kWMxfp4 ? SH::BN / 32 * 256 : 0;
-  static constexpr int L = SH::A_LOADS + B_LOADS + SC_LOADS;  // loads per wavefront per stage
-  static constexpr int STAGE = SH::A_BYTES + SH::BN * B_ROWB + SC_BYTES;
+  static constexpr int LB = B_LOADS + SC_LOADS;          // weight-side loads per wavefront
+  static constexpr int L = SH::A_LOADS + LB;             // loads per wavefront per stage
+  static constexpr int B_STAGE = SH::BN * B_ROWB + SC_BYTES;
   static_assert(WQ != kWMxfp4 || (SH::BK == 128 && SC_LOADS * 32 * SH::WAVES == SH::BN),
                 "MXFP4 stages hold 128 k: one scale dword per row");
-  static constexpr int LDS = SH::S * STAGE;
+  // LDS: S slots of the token-row tile, then SB slots of the weight tile
+  static constexpr int LDS = SH::S * SH::A_BYTES + SH::SB * B_STAGE;
   static_assert(B_LOADS * B_RPL * SH::WAVES == SH::BN, "load split");
-  static_assert(SH::S >= 2 && (SH::S - 2) * L < 64, "stages in flight fit the vmcnt counter");
+  // Each barrier issues the operand with fewer stages first (its step is needed sooner).  WAIT:
+  // the loads a wavefront issued after the token rows and weights of step lk + 1, when step lk
+  // waits for them.  PRO_WAIT: the loads of the prologue issued after those of step 0.
+  static constexpr int WAIT = SH::S == SH::SB ? (SH::S - 2) * L
+                              : SH::S < SH::SB ? LB : SH::A_LOADS;
+  static constexpr int PRO_WAIT = (SH::S - 2) * SH::A_LOADS + (SH::SB - 2) * LB;
+  static_assert(SH::S >= 2 && WAIT < 64 && PRO_WAIT < 64, "loads in flight fit the vmcnt counter");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-using PrefillShape = TileShape<256, 256, 2, 4, 2>;
+using PrefillShape = TileShape<256, 256, 2, 4, 2, 64, 3>;
 using DecodeShape = TileShape<32, 256, 1, 4, 4>;
 // FP8 weights halve the weight tile.  Decode: stages of 128 k (each weight row a whole 128-byte
 // line; with 64 k every line was fetched in two halves a k-step apart), two of them so that two
@@ -244,9 +259,14 @@ __device__ __forceinline__ TileLoc locate_tile(const GroupedGemm& p, int tile) {
   // that out, and slot 0 keeps the address in range if it ever happened
   t.w = p.group_slot && g < p.G_routed ? max(p.group_slot[g], 0) : g;
   t.row_base = row_base;
-  t.m0 = (rem % mt) * SH::BM;
+  // the group's 32-row blocks are spread evenly over its mt row tiles (each gets at most BM / 32
+  // of them, since mt = ceil(blocks / (BM / 32))), so no tile is a nearly empty remainder and
+  // the MFMAs of blocks past a tile's rows can be skipped without some tiles finishing far ahead
+  const int nb = (rows + 31) / 32, r = rem % mt;
+  const int b0 = (int)((int64_t)r * nb / mt), b1 = (int)((int64_t)(r + 1) * nb / mt);
+  t.m0 = b0 * 32;
   t.n_t = nblk * GN + rem / mt;
-  t.rows_here = min(SH::BM, rows - t.m0);
+  t.rows_here = min((b1 - b0) * 32, rows - t.m0);
   return t;
 }
 
@@ -378,12 +398,12 @@ __device__ __forceinline__ float4* tail_slot(const GroupedGemm& p, int xcd, int 
 template <class SH, int EPI, bool GATHER, int GN, int WQ>
 __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   using GE = Geo<SH, WQ>;
-  constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, L = GE::L;
+  constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, SB = SH::SB, L = GE::L;
   constexpr int TM = SH::TM, TN = SH::TN, KK = SH::KK, RPL = SH::RPL;
   constexpr int B_ROWB = GE::B_ROWB, B_RPL = GE::B_RPL, B_LOADS = GE::B_LOADS, B_CH = GE::B_CH;
   constexpr int ROWB = SH::ROWB, CH = SH::CH;
-  constexpr int STAGE = GE::STAGE, SC_LOADS = GE::SC_LOADS;
-  constexpr int SC_OFF = SH::A_BYTES + SH::BN * GE::B_ROWB;  // scale tile in a stage
+  constexpr int SC_LOADS = GE::SC_LOADS, B_STAGE = GE::B_STAGE;
+  constexpr int SC_OFF = SH::BN * GE::B_ROWB;  // scale tile in a weight stage
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs W1 and W3 blocks");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -403,7 +423,9 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int sw = row_swizzle<CH>(l32), swb = row_swizzle<B_CH>(l32);
   const uint32_t a_frag = (uint32_t)((wm * SH::WTM + l32) * ROWB);
-  const uint32_t b_frag = (uint32_t)(SH::A_BYTES + (wn * SH::WTN + l32) * B_ROWB);
+  const uint32_t b_frag = (uint32_t)((wn * SH::WTN + l32) * B_ROWB);
+  char* const a_slots = smem;                      // S slots of A_BYTES
+  char* const b_slots = smem + S * SH::A_BYTES;    // SB slots of B_STAGE
 
   struct Tile {
     TileLoc loc;
@@ -497,16 +519,20 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       b_off[i] = src < p.N ? row_at + c * 16 : kOutOfRange;
     }
   };
-  // local k-step lk of the current tile into LDS slot `slot`; lk >= ktn loads nothing
-  auto issue = [&](int lk, int slot) {
+  // local k-step lk of the current tile into LDS slots `slot` (token rows) and `bslot` (weights);
+  // lk >= ktn loads nothing
+  auto issue_a = [&](int lk, int slot) {
     const bool valid = lk < ktn;
-    char* sa = smem + slot * STAGE;
-    char* sb = sa + SH::A_BYTES;
+    char* sa = a_slots + slot * SH::A_BYTES;
     const int kb = valid ? (kt0 + lk) * ROWB : 0;
-    const int kbw = valid ? (kt0 + lk) * (WQ == kWMxfp4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i)
       load_lds16(rA, sa + (wid * SH::A_LOADS + i) * 1024, valid ? a_off[i] : kOutOfRange, kb);
+  };
+  auto issue_b = [&](int lk, int bslot) {
+    const bool valid = lk < ktn;
+    char* sb = b_slots + bslot * B_STAGE;
+    const int kbw = valid ? (kt0 + lk) * (WQ == kWMxfp4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int blk = wid * B_LOADS + i;
@@ -520,21 +546,38 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       for (int i = 0; i < SC_LOADS; ++i) {
         const int blk = wid * SC_LOADS + i;
         const bool second = EPI == EPI_SWIGLU && (blk & 1);
-        load_lds4(second ? rS2 : rS, sa + SC_OFF + blk * 256, valid ? s_off[i] : kOutOfRange, kbs);
+        load_lds4(second ? rS2 : rS, sb + SC_OFF + blk * 256, valid ? s_off[i] : kOutOfRange, kbs);
       }
     }
   };
-  auto prologue = [&]() {
+  // The step-lk barrier sends out the token rows of step lk + S and the weights of step lk + SB,
+  // the shallower operand first; the start of the k-loop sends steps S - 1 and SB - 1 in the same
+  // order, so the wait at every barrier is the constant GE::WAIT.
+  auto issue_both = [&](int la, int sa, int lb, int sb) {
+    if constexpr (S <= SB) {
+      issue_a(la, sa);
+      issue_b(lb, sb);
+    } else {
+      issue_b(lb, sb);
+      issue_a(la, sa);
+    }
+  };
+  auto prologue = [&]() {  // steps 0 .. S - 2 (token rows) and 0 .. SB - 2 (weights), by step
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue(s, s);
+    for (int s = 0; s < (S > SB ? S : SB) - 1; ++s) {
+      if (s < S - 1) issue_a(s, s);
+      if (s < SB - 1) issue_b(s, s);
+    }
   };
 
   f32x16 acc[TM][TN];
   bf16x8 fa[2][TM], fb[2][TN];
-  auto read_frags = [&](const char* st, int kk, int buf) {
+  // NV: the wavefront's token blocks that hold rows of the tile (the others are skipped)
+  auto read_frags = [&](auto nv, const char* sta, const char* st, int kk, int buf) {
+    constexpr int NV = decltype(nv)::value;
     const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8*)(st + a_frag + coff + i * 32 * ROWB);
+    for (int i = 0; i < NV; ++i) fa[buf][i] = *(const bf16x8*)(sta + a_frag + coff + i * 32 * ROWB);
     if constexpr (WQ == kWMxfp4) {
       // a k-sub's 16 codes are half of chunk kk / 2 of the 64-byte row; the lane takes 8 of them
       // (one dword) and the scale of their 32-block kk / 2
@@ -560,38 +603,42 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     }
   };
   // weights as the first operand: D[column][token]
-  auto mfmas = [&](int buf) {
+  auto mfmas = [&](auto nv, int buf) {
+    constexpr int NV = decltype(nv)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
   };
   // Every step issues L loads per wavefront (stage lk + S, masked past the end), so when step
   // lk waits for stage lk + 1 exactly S - 2 stages were issued after it.
-  auto kloop = [&]() {
-    read_frags(smem, 0, 0);
-    issue(S - 1, S - 1);
+  auto kloop = [&](auto nv) {
+    constexpr int NV = decltype(nv)::value;
+    read_frags(nv, a_slots, b_slots, 0, 0);
+    issue_both(S - 1, S - 1, SB - 1, SB - 1);
     for (int lk = 0; lk < ktn; ++lk) {
-      const char* cur = smem + (lk % S) * STAGE;
-      const char* nxt = smem + ((lk + 1) % S) * STAGE;
+      const char* cura = a_slots + (lk % S) * SH::A_BYTES;
+      const char* curb = b_slots + (lk % SB) * B_STAGE;
+      const char* nxta = a_slots + ((lk + 1) % S) * SH::A_BYTES;
+      const char* nxtb = b_slots + ((lk + 1) % SB) * B_STAGE;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         if (kk < KK - 1) {
-          read_frags(cur, kk + 1, (kk + 1) & 1);
+          read_frags(nv, cura, curb, kk + 1, (kk + 1) & 1);
         } else {
-          wait_vmcnt<(S - 2) * L>();  // stage lk + 1 landed (this wavefront's share)
-          wait_lgkmcnt<0>();          // this wavefront's reads of stage lk returned
-          barrier_keep_loads();       // ... and everyone else's
-          read_frags(nxt, 0, 0);
-          issue(lk + S, lk % S);
+          wait_vmcnt<GE::WAIT>();  // step lk + 1 landed (this wavefront's share)
+          wait_lgkmcnt<0>();       // this wavefront's reads of step lk returned
+          barrier_keep_loads();    // ... and everyone else's
+          read_frags(nv, nxta, nxtb, 0, 0);
+          issue_both(lk + S, lk % S, lk + SB, lk % SB);
         }
-        mfmas(kk & 1);
+        mfmas(nv, kk & 1);
         // interleave: one MFMA, then one LDS read and (after the barrier) one global load
 #pragma unroll
-        for (int m = 0; m < TM * TN; ++m) {
+        for (int m = 0; m < NV * TN; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (m < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (m < NV + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (kk == KK - 1 && m < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
@@ -611,9 +658,21 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    wait_vmcnt<(S - 2) * L>();  // stage 0 (and the previous tile's stores, issued after it)
+    wait_vmcnt<GE::PRO_WAIT>();  // step 0 (and the previous tile's stores, issued after it)
     barrier_keep_loads();
-    kloop();
+    // token blocks of this wavefront that hold rows: the two wavefronts of a SIMD split the
+    // tile's rows, so the SIMD's MFMA time follows the tile's real rows
+    const int nv = __builtin_amdgcn_readfirstlane(
+        min(TM, max(0, (cur.loc.rows_here - wm * SH::WTM + 31) / 32)));
+    if constexpr (TM == 4) {
+      if (nv == 4) kloop(std::integral_constant<int, 4>{});
+      else if (nv == 3) kloop(std::integral_constant<int, 3>{});
+      else if (nv == 2) kloop(std::integral_constant<int, 2>{});
+      else if (nv == 1) kloop(std::integral_constant<int, 1>{});
+      else kloop(std::integral_constant<int, 0>{});
+    } else {
+      kloop(std::integral_constant<int, TM>{});
+    }
     // everyone is done with the operand slots and the loads past the last stage have landed
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();
