@@ -202,7 +202,8 @@ def main():
     if mx:
         shape, rows = "TileShape<32,256,1,4,3,128>", "32-row tiles"
     elif (w.T * w.k) // w.E >= 128:
-        shape = "TileShape<256,256,2,4,2>"
+        shape = ("TileShape<256,256,2,4,2>" if fp8
+                 else "TileShape<256,256,2,4,2,64,3>")  # 2 token-row, 3 weight LDS stages
         rows = "256x256 tiles"
     else:
         shape = (("TileShape<32,256,1,4,2,128>" if w.H % 128 == 0 else "TileShape<32,256,1,4,3>")

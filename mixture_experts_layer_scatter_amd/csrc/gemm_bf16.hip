@@ -205,10 +205,12 @@ struct Geo {
   static_assert(B_LOADS * B_RPL * SH::WAVES == SH::BN, "load split");
   // Each barrier issues the operand with fewer stages first (its step is needed sooner).  WAIT:
   // the loads a wavefront issued after the token rows and weights of step lk + 1, when step lk
-  // waits for them.  PRO_WAIT: the loads of the prologue issued after those of step 0.
+  // waits for them (only loads are in flight inside the k-loop).  PRO_WAIT: the wait for step 0
+  // at the start of a tile; the previous tile's stores were issued after the prologue, so with
+  // S != SB it waits for everything rather than count on loads and stores completing in order.
   static constexpr int WAIT = SH::S == SH::SB ? (SH::S - 2) * L
                               : SH::S < SH::SB ? LB : SH::A_LOADS;
-  static constexpr int PRO_WAIT = (SH::S - 2) * SH::A_LOADS + (SH::SB - 2) * LB;
+  static constexpr int PRO_WAIT = SH::S == SH::SB ? (SH::S - 2) * L : 0;
   static_assert(SH::S >= 2 && WAIT < 64 && PRO_WAIT < 64, "loads in flight fit the vmcnt counter");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
