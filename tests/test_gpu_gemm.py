@@ -84,6 +84,7 @@ def _ffn_case(counts, H, I, dtype, seed=0):
     ([0, 1, 31, 33, 7, 0, 64, 2], 128, 192),          # small tiles, a column tail (192 = 128 + 64)
     ([300, 0, 513, 7, 256], 256, 320),                 # 256-row tiles, ragged tails
     ([1024, 1000, 1050, 990], 512, 256),
+    ([129, 257, 385, 128], 256, 256),                 # 32-row blocks spread over row tiles: 5 | 4+5 | 6+7
     ([17] * 40, 1024, 128),
 ])
 def test_expert_ffn_bf16(counts, H, I):
