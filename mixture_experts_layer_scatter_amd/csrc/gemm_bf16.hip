@@ -237,21 +237,31 @@ struct TileLoc {
   int w;  // index of the group's weights in b / b2 / the scales (its slot when group_slot is set)
 };
 
+// An int32 at a uniform index of a table that earlier kernels wrote (the tile map, the group
+// offsets, the expert -> slot table): a scalar load through the scalar cache, which keeps the
+// tile-to-tile lookups off the vector-memory path (whose loads would each wait for every load
+// and store in flight) and, after the first tile, hits in the scalar cache.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* a, int i) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  return ((cptr)a)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // tile `tile` of the (unsplit) tile list: its group, row block and column block
 template <class SH, int GN>
 __device__ __forceinline__ TileLoc locate_tile(const GroupedGemm& p, int tile) {
   int g = 0, row_base = 0, rows = p.static_rows, li = tile;
+  tile = __builtin_amdgcn_readfirstlane(tile);
   if (p.tile_start) {
     int lo = 0, hi2 = p.G;  // largest g with tile_start[g] <= tile
     while (hi2 - lo > 1) {
       const int mid = (lo + hi2) >> 1;
-      if (p.tile_start[mid] <= tile) lo = mid;
+      if (ld_uniform(p.tile_start, mid) <= tile) lo = mid;
       else hi2 = mid;
     }
     g = lo;
-    li = tile - p.tile_start[g];
-    row_base = p.offsets[g];
-    rows = p.offsets[g + 1] - row_base;
+    li = tile - ld_uniform(p.tile_start, g);
+    row_base = ld_uniform(p.offsets, g);
+    rows = ld_uniform(p.offsets, g + 1) - row_base;
   }
   const int mt = (rows + SH::BM - 1) / SH::BM;
   const int nblk = li / (mt * GN), rem = li % (mt * GN);
@@ -259,7 +269,7 @@ __device__ __forceinline__ TileLoc locate_tile(const GroupedGemm& p, int tile) {
   t.g = g;
   // a slot of -1 would mean a group with rows whose weights are not resident; the caller rules
   // that out, and slot 0 keeps the address in range if it ever happened
-  t.w = p.group_slot && g < p.G_routed ? max(p.group_slot[g], 0) : g;
+  t.w = p.group_slot && g < p.G_routed ? max(ld_uniform(p.group_slot, g), 0) : g;
   t.row_base = row_base;
   // the group's 32-row blocks are spread evenly over its mt row tiles (each gets at most BM / 32
   // of them, since mt = ceil(blocks / (BM / 32))), so no tile is a nearly empty remainder and
@@ -413,7 +423,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   const int wm = wid / WN, wn = wid % WN;
   const int K = p.K, KT = K / SH::BK;
   const int NT = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  const int total_base = p.tile_start ? p.tile_start[p.G] : (p.static_rows + BM - 1) / BM * NT;
+  const int total_base =
+      p.tile_start ? ld_uniform(p.tile_start, p.G) : (p.static_rows + BM - 1) / BM * NT;
   // split-K: ksplit consecutive copies of the tile list; copy ks reduces over its share of the
   // k-steps into the partial output c + ks * c_split_stride
   const int ks_n = p.ksplit > 1 ? p.ksplit : 1;
@@ -496,17 +507,20 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
                                           : kOutOfRange;
       }
     }
+    // the gathered row indices are read for every lane (rows past the tile's end read its last
+    // row and are masked afterwards), so the loads go out together and are waited for once
+    int a_src[SH::A_LOADS];
+#pragma unroll
+    for (int i = 0; i < SH::A_LOADS; ++i) {
+      const int r = (wid * SH::A_LOADS + i) * RPL + lane / CH;
+      const int prow = t.loc.row_base + t.loc.m0 + min(r, t.loc.rows_here - 1);
+      a_src[i] = GATHER ? p.row_map[prow] : prow;
+    }
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i) {
       const int r = (wid * SH::A_LOADS + i) * RPL + lane / CH;
       const int c = (lane % CH) ^ row_swizzle<CH>(r);
-      uint32_t off = kOutOfRange;
-      if (r < t.loc.rows_here) {
-        const int prow = t.loc.row_base + t.loc.m0 + r;
-        const int64_t src = GATHER ? (int64_t)p.row_map[prow] : (int64_t)prow;
-        off = (uint32_t)(src * K * 2) + c * 16;
-      }
-      a_off[i] = off;
+      a_off[i] = r < t.loc.rows_here ? (uint32_t)((int64_t)a_src[i] * K * 2) + c * 16 : kOutOfRange;
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -715,7 +729,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_tail_kernel(GroupedGemm p, i
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wid / SH::WN, wn = wid % SH::WN;
   const int xcd = blockIdx.x % 8, t = (blockIdx.x / 8) % kTailPieces, ib = blockIdx.x / (8 * kTailPieces);
-  const TailPlan plan = tail_plan(p.tile_start[p.G], xcd, nx, p.K / SH::BK, true);
+  const TailPlan plan = tail_plan(ld_uniform(p.tile_start, p.G), xcd, nx, p.K / SH::BK, true);
   if (plan.pieces <= 1 || t >= plan.tail) return;
   f32x16 acc[TM][TN];
 #pragma unroll
