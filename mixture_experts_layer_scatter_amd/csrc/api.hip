@@ -26,14 +26,18 @@ struct Layout {
 int elem_bytes(const moe_dims_t* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 
 // Split-K factor of the fused layer's bf16 gate: enough workgroups to fill the GPU when there
-// are few (token, expert) tiles, keeping at least 4 k-steps per split.
+// are few (token, expert) tiles, keeping at least 4 k-steps per split.  With 128-row tiles
+// (one 128-KB-LDS workgroup per CU) it aims at one workgroup per CU, since every split adds
+// T x E fp32 partial sums to write and reduce.
 int gate_splits(const moe_dims_t* d) {
   if (d->dtype != MOE_BF16 || d->T <= 0) return 1;
   const int bn = d->E <= 32 ? 32 : d->E <= 64 ? 64 : d->E <= 128 ? 128 : 256;
-  const int64_t tiles = (int64_t)ceil_div(d->T, 32) * ceil_div(d->E, bn);
+  const int bm = gemm_gate_bm(d->T, d->E, true);
+  const int64_t tiles = (int64_t)ceil_div(d->T, bm) * ceil_div(d->E, bn);
+  const int64_t limit = bm == 128 ? 256 : 1024;
   const int kt = d->H / 64;
   int s = 1;
-  while (s < 16 && tiles * s * 2 <= 1024 && kt / (s * 2) >= 4) s *= 2;
+  while (s < 16 && tiles * s * 2 <= limit && kt / (s * 2) >= 4) s *= 2;
   return s;
 }
 

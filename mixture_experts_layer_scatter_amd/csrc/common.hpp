@@ -131,6 +131,8 @@ constexpr int kTailPieces = 32;  // partial tiles per XCD the tail buffer holds
 enum GemmKind { GEMM_GATE = 0, GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
 // tiles per group needed by the chosen configuration
 void gemm_bf16_tiling(GemmKind kind, int max_rows_per_group, int N, int* bm, int* nt);
+// rows of a bf16 gate tile for T tokens and E experts, split reduction or not
+int gemm_gate_bm(int T, int E, bool split);
 hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& g, int max_rows_per_group,
                             int num_cus, hipStream_t s);
 // bytes of GroupedGemm::tail_part needed by launch_gemm_bf16 for this kind and group size

@@ -784,7 +784,15 @@ static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStrea
   return hipGetLastError();
 }
 
-// choose tiles for a kind of GEMM from the rows a group holds on average
+// Rows of a gate tile.  Every tile reads the whole [E, H] gate weight through LDS, so with
+// 32-row tiles the weight's L2 -> LDS traffic is E / 32 times the tokens' (4x at 128 experts);
+// 128-row tiles cut it to a quarter.  They are taken when the reduction is split (so that
+// there are still enough workgroups) over many tokens and 64-128 experts.
+int gemm_gate_bm(int T, int E, bool split) {
+  return split && T >= 2048 && E > 32 && E <= 128 ? 128 : 32;
+}
+
+// choose tiles for a kind of GEMM from the rows a group holds on average (the gate: its tokens)
 void gemm_bf16_tiling(GemmKind kind, int avg_rows_per_group, int N, int* bm, int* nt) {
   if (kind == GEMM_GATE) {
     const int bn = N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
@@ -810,6 +818,7 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   int bm, nt;
   gemm_bf16_tiling(kind, avg_rows_per_group, p.N, &bm, &nt);
   if (p.ksplit > 1 && kind != GEMM_GATE) return hipErrorInvalidValue;  // fp32 output only
+  if (kind == GEMM_GATE) bm = gemm_gate_bm(p.static_rows, p.N, p.ksplit > 1);
   // upper bound of the tile count (the exact count is on the device)
   int64_t max_tiles;
   if (p.tile_start) {
@@ -821,6 +830,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   if (max_tiles > (1 << 30)) max_tiles = 1 << 30;
   const int mt = (int)max_tiles;
   if (kind == GEMM_GATE) {
+    if (bm == 128) {  // wavefront tiles of 64 tokens x 32 or 64 experts
+      if (p.N <= 64) return run<TileShape<128, 64, 2, 2, 4>, EPI_F32, false, 1>(p, mt, num_cus, s);
+      return run<TileShape<128, 128, 2, 2, 4>, EPI_F32, false, 1>(p, mt, num_cus, s);
+    }
     if (p.N <= 32) return run<TileShape<32, 32, 1, 1, 4>, EPI_F32, false, 1>(p, mt, num_cus, s);
     if (p.N <= 64) return run<TileShape<32, 64, 1, 2, 4>, EPI_F32, false, 1>(p, mt, num_cus, s);
     if (p.N <= 128) return run<TileShape<32, 128, 1, 4, 4>, EPI_F32, false, 1>(p, mt, num_cus, s);

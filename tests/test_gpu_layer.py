@@ -161,6 +161,14 @@ def _random_workloads(n=14, seed=2024):
     return out
 
 
+@pytest.mark.parametrize("E,H", [(100, 512), (40, 1024)])
+def test_split_gate_128_row_tiles(E, H):
+    """T >= 2048 tokens over 33-128 experts: the fused layer's gate splits its reduction and
+    takes 128-row tiles; T = 2100 leaves a ragged last row tile and E a column tail."""
+    need_gpu()
+    check_layer(moe_synth.Workload(f"gate128_E{E}", 130 + E, T=2100, H=H, E=E, k=2, I=64))
+
+
 @pytest.mark.parametrize("w", _random_workloads(), ids=lambda w: (
     f"{w.name}-{w.dtype}-T{w.T}-H{w.H}-E{w.E}-k{w.k}-I{w.I}-Is{w.I_shared}-cf{w.capacity_factor}"
     f"-z{w.zipf_s}-r{w.renormalize}-b{w.bias_mode}"))
