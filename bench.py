@@ -251,13 +251,20 @@ def main():
 
 
 def kernel_source_digest():
-    """sha256 over the sources the grouped GEMM kernel is built from."""
+    """sha256 over the code of the sources the grouped GEMM kernel is built from.
+
+    Line comments, trailing blanks and empty lines are left out, so that editing a comment
+    does not mark the committed counters stale; any change to the code does.
+    """
     import hashlib
 
     h = hashlib.sha256()
     for f in ("gemm_bf16.hip", "common.hpp", "api.hip"):
-        with open(os.path.join(ROOT, "mixture_experts_layer_scatter_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mixture_experts_layer_scatter_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -8,12 +8,13 @@
 // W3 x)).  "MoE 推理架构深度实战：从 Expert Parallelism 到 DeepSeek-V3 的工程落地"
 // §2.1: the gate is a linear map from hidden size to experts without bias.
 //
-// One kernel template serves all three (gemm_kernel), in two shapes:
+// One kernel template serves all three (gemm_kernel), in these shapes:
 //  * prefill (a group holds >= 128 rows on average): 256 x 256 tiles, 8
 //    wavefronts (two per SIMD, each 128 token rows x 64 columns), two LDS
-//    stages (128 KB);
+//    slots for the token-row tile and three for the weight tile (160 KB);
 //  * decode and the gate: 32-row tiles, up to 4 wavefronts across the columns,
-//    four LDS stages to keep weight bytes in flight.
+//    four LDS stages to keep weight bytes in flight;
+//  * a split gate over many tokens: 128-row tiles, 4 wavefronts of 64 rows.
 //
 // Design for gfx950:
 //  * C[r, n] = sum_k A[r, k] * B[n, k]; both operands are contiguous along k,
@@ -28,15 +29,18 @@
 //    c of row r is stored at chunk c ^ swz(r), so the rows one fragment read
 //    serves per cycle fall in distinct banks.
 //  * At the barrier in the middle of step kt every wavefront has read all of
-//    stage kt, whose slot then takes stage kt + S right away; the barrier is a
-//    bare s_barrier that leaves the S - 1 stages in flight alone (a full
-//    __syncthreads would drain them).  Loads past the last stage carry the
-//    out-of-range offset (no memory access, zeros into a free slot), so every
-//    step issues the same number of loads and the wait count is a constant.
+//    stage kt, whose slots then take the token rows of step kt + S and the
+//    weights of step kt + SB right away; the barrier is a bare s_barrier that
+//    leaves the stages in flight alone (a full __syncthreads would drain them).
+//    Loads past the last stage carry the out-of-range offset (no memory access,
+//    zeros into a free slot), so every step issues the same number of loads and
+//    the wait count is a constant.
 //  * Buffer loads return zero past the resource's size and for the
 //    out-of-range offset used for rows beyond a group: ragged row tails and
-//    column tails need no branches.  Every tile costs the same, which keeps the
-//    workgroups of an XCD in step over the operand panels they share.
+//    column tails need no branches.  A group's 32-row blocks are spread evenly
+//    over its row tiles and a wavefront skips the MFMAs of blocks without rows,
+//    so the tiles of a group cost about the same, which keeps the workgroups of
+//    an XCD in step over the operand panels they share.
 //  * Groups (experts) have ragged row counts known only on the device.  A
 //    device tile map (tile_start) lists every group's tiles; a persistent grid
 //    walks it.  Tiles are dealt out XCD by XCD (workgroups go round-robin over
