@@ -161,6 +161,16 @@ def _random_workloads(n=14, seed=2024):
     return out
 
 
+@pytest.mark.parametrize("cf", [None, 1.0])
+def test_max_experts_every_token(cf):
+    """E = 1024 routed experts (the most the routing kernels take), k = 8, with an always-on
+    shared expert of the routed width folded in as group 1025; capacity factor 1.0 keeps
+    floor(600 * 8 / 1024) = 4 rows per expert and drops the rest."""
+    need_gpu()
+    check_layer(moe_synth.Workload("max_experts", 140 + (cf is not None), T=600, H=128, E=1024,
+                                   k=8, I=64, I_shared=64, capacity_factor=cf))
+
+
 @pytest.mark.parametrize("E,H", [(100, 512), (40, 1024)])
 def test_split_gate_128_row_tiles(E, H):
     """T >= 2048 tokens over 33-128 experts: the fused layer's gate splits its reduction and
