@@ -121,12 +121,27 @@ def main():
     counts = torch.empty(w.E, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
-    step(dict(counts=counts, n_dropped=nd, topk_ids=ids))
+    lg = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+    step(dict(counts=counts, n_dropped=nd, topk_ids=ids, logits=lg))
     torch.cuda.synchronize()
     cnt = counts.cpu().numpy().astype(np.int64)
     R = int(cnt.sum())
     touched = int((cnt > 0).sum())
     n_dropped = int(nd.item())
+    # near ties of this routing: tokens whose k-th and (k+1)-th selection keys (the GPU's fp32
+    # logits plus the bias, one fp32 add) are less than 1e-6 apart, where a different rounding
+    # of the gate could change the selected experts
+    keys = lg.cpu().numpy()
+    if t["bias"] is not None:
+        keys = keys + t["bias"].cpu().numpy()[None, :]
+    del lg
+    if w.k < w.E:
+        top = -np.partition(-keys, (w.k - 1, w.k), axis=1)
+        margin = top[:, w.k - 1].astype(np.float64) - top[:, w.k].astype(np.float64)
+        near_ties = int((margin < 1e-6).sum())
+        min_margin = float(margin.min()) if len(margin) else None
+    else:
+        near_ties, min_margin = 0, None
 
     for _ in range(args.warmup):
         step()
@@ -240,6 +255,8 @@ def main():
                   "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
                   "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
                   "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
+                  "near_tie_tokens": near_ties,
+                  "min_topk_margin": None if min_margin is None else float(f"{min_margin:.3g}"),
                   "load_stats": load,
                   **({"lowbit_vs_bf16_weights_rel_l2": round(quant_err, 5)} if lowbit else {}),
                   **({"expert_cache": cache_res} if cache_res is not None else {})},
