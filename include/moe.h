@@ -65,7 +65,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  *  §2.1); 0 = keep the raw softmax probabilities.
  *  bias_mode (moe_bias_mode_t): how a routing bias, when one is given, enters.
  *  Supported: bf16 needs H % 64 == 0, I % 64 == 0 and I_shared % 64 == 0;
- *  fp32 needs H % 4 == 0.  T * k must fit in int32. */
+ *  fp32 needs H % 4 == 0.  T * k must fit in int32.  The bf16 kernels address
+ *  operands with 32-bit byte offsets, so there the packed rows ((T*k + T) x H
+ *  and x max(I, I_shared)), x, the gate weight and one expert's matrix must
+ *  each stay below 2^31 bytes; larger sizes return MOE_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t T, H, E, k, I;
   int32_t I_shared;
