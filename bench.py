@@ -215,7 +215,7 @@ def main():
     # the library takes 256-row tiles when a group holds >= 128 rows on average
     # (the timed span is the grouped GEMM plus the reduction of its split last round of tiles)
     if mx:
-        shape, rows = "TileShape<32,256,1,4,3,128>", "32-row tiles"
+        shape, rows = "TileShape<32,256,1,4,2,128>", "32-row tiles"
     elif (w.T * w.k) // w.E >= 128:
         shape = ("TileShape<256,256,2,4,2>" if fp8
                  else "TileShape<256,256,2,4,2,64,3>")  # 2 token-row, 3 weight LDS stages
