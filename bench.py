@@ -147,18 +147,22 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: events around the dominant kernel on the launch stream
+    # timed region: events around the dominant kernel and around the whole layer, on the launch
+    # stream (the layer's per-step spans give the median and the minimum next to the mean)
     dom = (_lib.EV_PERMUTE, _lib.EV_GATE_UP)
     pairs = [(Event(), Event()) for _ in range(args.steps)]
+    spans = [(Event(), Event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in pairs:
+    for (a, b), (c, e) in zip(pairs, spans):
         ev = [None] * _lib.NUM_EVENTS
         ev[dom[0]], ev[dom[1]] = a.handle.value, b.handle.value
+        ev[_lib.EV_START], ev[_lib.EV_END] = c.handle.value, e.handle.value
         step(dict(events=ev))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gu_ms = [a.elapsed_ms(b) for a, b in pairs]
+    layer_ms = [c.elapsed_ms(e) for c, e in spans]
     ms_per_step = wall * 1e3 / args.steps
 
     # per-stage breakdown (untimed extra steps)
@@ -251,6 +255,8 @@ def main():
                    **({"expert_weights": "mxfp4_e2m1_e8m0_per_32"} if mx else {})},
         "roofline": roof,
         "layer": {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
+                  "ms_median": round(float(np.median(layer_ms)), 4),
+                  "ms_min": round(float(np.min(layer_ms)), 4),
                   "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
                   "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
                   "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
