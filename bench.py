@@ -234,6 +234,9 @@ def main():
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
     layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count, "hip": torch.version.hip}
 
     out = {
         "metric": METRIC,
@@ -248,6 +251,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded normal draws, shapes of the named workload)",
+        "device": device,
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "I_shared": Is, "capacity": cap, "accumulate": "fp32",
                    **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {}),
