@@ -75,8 +75,30 @@ def routing(w: moe_synth.Workload, x=None, logits=None):
     return dict(logits=logits, ids=ids, w=wts, margin=margin, capacity=cap, **perm)
 
 
+def _experts_ahead(weights: Weights, experts, window: int = 16):
+    """(e, weights.expert(e)) for each e in order, drawn up to `window` experts ahead in
+    threads (NumPy's generators and the oracle's C calls release the GIL)."""
+    from collections import deque
+    from concurrent.futures import ThreadPoolExecutor
+
+    experts = list(experts)
+    with ThreadPoolExecutor(min(window, 16)) as ex:
+        q = deque()
+        it = iter(experts)
+        for e in it:
+            q.append((e, ex.submit(weights.expert, e)))
+            if len(q) >= window:
+                break
+        while q:
+            e, f = q.popleft()
+            nxt = next(it, None)
+            if nxt is not None:
+                q.append((nxt, ex.submit(weights.expert, nxt)))
+            yield e, f.result()
+
+
 def layer_tokens(w: moe_synth.Workload, x, route, tokens, weights: Weights, shared=None):
-    """float64 outputs y[tokens] of the layer, given the oracle's full routing.
+    """float64 outputs y[tokens] of the layer, given a full routing (ids, w, pos).
 
     Runs each needed expert only on the selected tokens' kept slots and sums in
     slot order (oracle.combine); the always-on expert is added when present.
@@ -93,9 +115,9 @@ def layer_tokens(w: moe_synth.Workload, x, route, tokens, weights: Weights, shar
         for j in range(k):
             if pos[i, j] >= 0:
                 need.setdefault(int(ids[i, j]), []).append((i, j))
-    for e, lst in sorted(need.items()):
-        w1, w3, w2 = weights.expert(e)
-        rows = np.stack([x[tokens[i]] for (i, j) in lst])
+    for e, (w1, w3, w2) in _experts_ahead(weights, sorted(need)):
+        lst = need[e]
+        rows = x[tokens[[i for (i, j) in lst]]]
         out = oracle.expert_ffn(rows, w1, w3, w2)
         for r, (i, j) in enumerate(lst):
             yp[i * k + j] = out[r]

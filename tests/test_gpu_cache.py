@@ -5,7 +5,8 @@
   weights bit for bit.
 * Layer: the cached layer's output equals moe_layer_forward's bit for bit (the same kernels
   read the same weight values from other addresses), over a sequence of batches whose routing
-  changes, with evictions.
+  changes, with evictions; and one cached call, with experts in slots other than their ids,
+  against the oracle directly.
 """
 import numpy as np
 import pytest
@@ -113,3 +114,34 @@ def test_cached_layer_bit_exact(E, slots, T, k, shared):
     log(f"  over 16 batches: {total}")
     assert total["evictions"] > 0 and total["hits"] > 0
     cache.close()
+
+
+def test_cached_layer_against_oracle():
+    """One cached layer call checked straight against the oracle, with the routed experts in
+    slots that a prefetch filled out of id order (slot != expert id)."""
+    need_gpu()
+    import moe_synth
+    from layer_check import check_against_oracle, run_layer
+    from moe_synth.device import workload_tensors
+    from oracle_steps import Weights
+    w = moe_synth.Workload("cache_oracle", 210, T=200, H=256, E=16, k=2, I=128, zipf_s=1.2)
+    t = workload_tensors(w)
+    d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
+    cache = moe.ExpertCache(d, w.E, *(_pinned_from(t[k]) for k in ("w1", "w3", "w2")))
+    copy = torch.cuda.Stream()
+    cache.load([13, 2, 9, 0, 15], copy_stream=copy)
+    torch.cuda.synchronize()
+    # missing experts load in ascending id order into the lowest free slots
+    assert [cache.slots().tolist()[e] for e in (0, 2, 9, 13, 15)] == [0, 1, 2, 3, 4]
+    g = run_layer(w, lambda dd, dbg: moe.layer_forward_cached(dd, t["x"], t["wg"], t["bias"], cache,
+                                                             None, debug=dbg, copy_stream=copy)[0])
+    slot_of = cache.slots().tolist()
+    cache.close()
+    assert any(s >= 0 and s != e for e, s in enumerate(slot_of))
+    check_against_oracle(w, g, Weights(w, cache=False), None, tag=" (cached)")
+
+
+def _pinned_from(t):
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h

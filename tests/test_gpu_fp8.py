@@ -9,15 +9,14 @@ moe_layer_forward_fp8.
   accumulation order and the bf16 storage of the activation and the outputs, as in the bf16
   path: the same 2e-2 relative-L2 bar applies.
 """
-import dataclasses
-
 import numpy as np
 import pytest
 import torch
 
 import moe_synth
 import oracle
-from gpu_util import bf16_normal, bits, dev, f64, log, need_gpu, rel_l2
+from layer_check import check_against_oracle, run_layer
+from gpu_util import split_tail_pieces, bf16_normal, bits, dev, f64, log, need_gpu, rel_l2
 from oracle_steps import Fp8Weights, fp8_dequantised, layer_tokens, routing
 from moe_synth.device import workload_tensors
 
@@ -98,12 +97,28 @@ def _ffn_fp8_case(counts, H, I, seed=0):
     ([8] * 64, 1024, 512),                             # decode-like: many small groups
     ([300, 0, 513, 7, 256], 256, 320),                 # 256-row tiles, ragged tails
     ([1024, 1000, 1050, 990], 512, 256),
-    ([300, 280, 270, 310], 2048, 1024),                # the split last round of tiles
 ])
 def test_expert_ffn_fp8(counts, H, I):
     need_gpu()
     log(f"expert_ffn fp8 counts={counts[:8]} H={H} I={I}")
     got, ref = _ffn_fp8_case(counts, H, I, seed=len(counts) + H)
+    err = rel_l2(got, ref)
+    row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    log(f"  rel-L2 {err:.3g}, worst row {row_err.max():.3g}")
+    assert err <= 2e-2
+    assert (row_err <= 2e-2).all()
+
+
+def test_expert_ffn_fp8_split_tail():
+    """256 x 256 tiles on FP8 weights whose last, partly filled round of tiles is cut into
+    k-ranges in both GEMMs (the schedule mirrored in split_tail_pieces)."""
+    need_gpu()
+    counts, H, I = [520] * 6, 4096, 2048
+    gu = split_tail_pieces(counts, H, (I + 127) // 128)
+    dn = split_tail_pieces(counts, I, (H + 255) // 256)
+    log(f"expert_ffn fp8 (split tail round): pieces per XCD gate-up {gu}, down {dn}")
+    assert max(gu) > 1 and max(dn) > 1
+    got, ref = _ffn_fp8_case(counts, H, I, seed=11)
     err = rel_l2(got, ref)
     row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
     log(f"  rel-L2 {err:.3g}, worst row {row_err.max():.3g}")
@@ -120,36 +135,24 @@ def _quantized_tensors(t):
     return q, sh
 
 
-def check_layer_fp8(w, n_sample=None, seed=0):
+def check_layer_fp8(w):
+    """The fused layer on FP8 expert weights against the oracle on the same codes
+    dequantised, every token, with the step-by-step protocol of layer_check.py."""
     log(f"fp8 layer {w.name} T={w.T}: uploading and quantising")
     t = workload_tensors(w, log=log)
-    q, sh = _quantized_tensors(t)
-    cap = -1 if w.capacity_factor is None else moe.capacity(w.T, w.k, w.E, w.capacity_factor)
-    d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, I_shared=w.I_shared, capacity=cap,
-                 renormalize=w.renormalize, dtype=w.dtype)
-    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    pos = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    y = moe.layer_forward_fp8(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"], q["w2"], sh,
-                              debug=dict(topk_ids=ids, pos=pos))
+    q = {k: moe.quantize_fp8(t[k]) for k in ("w1", "w3", "w2")}
+    sh = None if t["shared"] is None else tuple(moe.quantize_fp8(a) for a in t["shared"])
+    for k in ("w1", "w3", "w2"):
+        t[k] = None
     torch.cuda.synchronize()
-    g_ids, g_pos, gy = ids.cpu().numpy(), pos.cpu().numpy(), f64(y)
+    g = run_layer(w, lambda d, dbg: moe.layer_forward_fp8(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"],
+                                                    q["w2"], sh, debug=dbg))
     del t, q, sh
     torch.cuda.empty_cache()
-    x = moe_synth.x(w)
-    r = routing(w, x)
-    agree = ((g_ids == r["ids"]) & ((g_pos >= 0) == (r["pos"] >= 0))).all(1)
-    rng = np.random.default_rng(seed)
-    tokens = np.arange(w.T) if n_sample is None else np.sort(rng.choice(w.T, n_sample, replace=False))
-    tokens = tokens[agree[tokens]]
     shared = None
     if w.I_shared:
         shared = tuple(fp8_dequantised(a) for a in moe_synth.shared_weights(w))
-    log(f"  oracle FFN (FP8 weights, dequantised) on {len(tokens)} tokens")
-    ref = layer_tokens(w, x, r, tokens, Fp8Weights(w, cache=False), shared)
-    err = rel_l2(gy[tokens], ref)
-    log(f"  rel-L2 {err:.3g} over {len(tokens)} tokens")
-    assert len(tokens) > 0
-    assert err <= 2e-2
+    check_against_oracle(w, g, Fp8Weights(w, cache=False), shared, tag=" (fp8)")
 
 
 @pytest.mark.parametrize("name,T", [("dsv3_decode", 24), ("qwen3_prefill", 160),
@@ -159,9 +162,9 @@ def test_layer_fp8_reduced_tokens_every_token(name, T):
     check_layer_fp8(moe_synth.get(name).scaled(T))
 
 
-def test_layer_fp8_full_size_decode_sampled():
+def test_layer_fp8_full_size_decode_every_token():
     need_gpu()
-    check_layer_fp8(moe_synth.get("dsv3_decode"), n_sample=6, seed=3)
+    check_layer_fp8(moe_synth.get("dsv3_decode"))
 
 
 def test_layer_fp8_shared_expert_of_another_width():

@@ -15,7 +15,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_util import bf16_normal, bits, dev, f64, log, need_gpu, rel_l2
+from gpu_util import split_tail_pieces, bf16_normal, bits, dev, f64, log, need_gpu, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -99,12 +99,16 @@ def test_expert_ffn_bf16(counts, H, I):
 
 
 @pytest.mark.parametrize("counts,H,I", [
-    ([300, 280, 270, 310], 2048, 1024),   # the last, partly filled round of tiles is split
-    ([700, 1, 650, 515], 1024, 2048),     # over k-ranges and added back by a second kernel
+    ([520] * 6, 4096, 2048),   # the last, partly filled round of tiles of both GEMMs is split
+    ([530, 512, 600, 515, 520, 700], 4096, 2048),   # over k-ranges, added back by a second kernel
 ])
 def test_expert_ffn_bf16_split_tail(counts, H, I):
     need_gpu()
-    log(f"expert_ffn bf16 (split tail round) counts={counts} H={H} I={I}")
+    gu = split_tail_pieces(counts, H, (I + 127) // 128)
+    dn = split_tail_pieces(counts, I, (H + 255) // 256)
+    log(f"expert_ffn bf16 (split tail round) counts={counts} H={H} I={I}: pieces per XCD "
+        f"gate-up {gu}, down {dn}")
+    assert max(gu) > 1 and max(dn) > 1
     got, ref = _ffn_case(counts, H, I, "bf16", seed=7)
     err = rel_l2(got, ref)
     row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)

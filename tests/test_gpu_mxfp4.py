@@ -15,6 +15,7 @@ import torch
 
 import moe_synth
 import oracle
+from layer_check import check_against_oracle, run_layer
 from gpu_util import bf16_normal, dev, f64, log, need_gpu, rel_l2
 from oracle_steps import Mxfp4Weights, layer_tokens, mxfp4_dequantised, routing
 from moe_synth.device import workload_tensors
@@ -114,37 +115,24 @@ def test_expert_ffn_mxfp4(counts, H, I):
     assert (row_err <= 2e-2).all()
 
 
-def check_layer_mxfp4(w, n_sample=None, seed=0):
+def check_layer_mxfp4(w):
+    """The fused layer on MXFP4 expert weights against the oracle on the same codes
+    dequantised, every token, with the step-by-step protocol of layer_check.py."""
     log(f"mxfp4 layer {w.name} T={w.T}: uploading and quantising")
     t = workload_tensors(w, log=log)
     q = {k: moe.quantize_mxfp4(t[k]) for k in ("w1", "w3", "w2")}
     sh = None if t["shared"] is None else tuple(moe.quantize_mxfp4(a) for a in t["shared"])
-    cap = -1 if w.capacity_factor is None else moe.capacity(w.T, w.k, w.E, w.capacity_factor)
-    d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, I_shared=w.I_shared, capacity=cap,
-                 renormalize=w.renormalize, dtype=w.dtype)
-    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    pos = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    y = moe.layer_forward_mxfp4(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"], q["w2"], sh,
-                                debug=dict(topk_ids=ids, pos=pos))
+    for k in ("w1", "w3", "w2"):
+        t[k] = None
     torch.cuda.synchronize()
-    g_ids, g_pos, gy = ids.cpu().numpy(), pos.cpu().numpy(), f64(y)
+    g = run_layer(w, lambda d, dbg: moe.layer_forward_mxfp4(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"],
+                                                    q["w2"], sh, debug=dbg))
     del t, q, sh
     torch.cuda.empty_cache()
-    x = moe_synth.x(w)
-    r = routing(w, x)
-    agree = ((g_ids == r["ids"]) & ((g_pos >= 0) == (r["pos"] >= 0))).all(1)
-    rng = np.random.default_rng(seed)
-    tokens = np.arange(w.T) if n_sample is None else np.sort(rng.choice(w.T, n_sample, replace=False))
-    tokens = tokens[agree[tokens]]
     shared = None
     if w.I_shared:
         shared = tuple(mxfp4_dequantised(a) for a in moe_synth.shared_weights(w))
-    log(f"  oracle FFN (MXFP4 weights, dequantised) on {len(tokens)} tokens")
-    ref = layer_tokens(w, x, r, tokens, Mxfp4Weights(w, cache=False), shared)
-    err = rel_l2(gy[tokens], ref)
-    log(f"  rel-L2 {err:.3g} over {len(tokens)} tokens")
-    assert len(tokens) > 0
-    assert err <= 2e-2
+    check_against_oracle(w, g, Mxfp4Weights(w, cache=False), shared, tag=" (mxfp4)")
 
 
 @pytest.mark.parametrize("name,T", [("dsv3_decode", 24), ("qwen3_prefill", 160),
@@ -154,9 +142,9 @@ def test_layer_mxfp4_reduced_tokens_every_token(name, T):
     check_layer_mxfp4(moe_synth.get(name).scaled(T))
 
 
-def test_layer_mxfp4_full_size_decode_sampled():
+def test_layer_mxfp4_full_size_decode_every_token():
     need_gpu()
-    check_layer_mxfp4(moe_synth.get("dsv3_decode"), n_sample=6, seed=4)
+    check_layer_mxfp4(moe_synth.get("dsv3_decode"))
 
 
 def test_layer_mxfp4_shared_expert_of_another_width():

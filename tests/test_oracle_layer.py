@@ -54,7 +54,10 @@ def test_textbook_dense_swiglu_when_one_expert():
 
 
 def _dense_reference(w, x, W, shared=None):
-    """NumPy gate + brute routing + SciPy softmax + buckets + dense mask."""
+    """NumPy gate + brute routing + SciPy softmax + buckets + dense mask.
+
+    With the bias in ranking-only mode the weights are the softmax of the bare logits at the
+    picked experts; otherwise the softmax of the biased keys."""
     X = moe_synth.widen(x)
     logits = (X @ moe_synth.widen(moe_synth.gate_weight(w)).T).astype(np.float32)
     bias = moe_synth.logit_bias(w)
@@ -62,7 +65,7 @@ def _dense_reference(w, x, W, shared=None):
     T = x.shape[0]
     cap = -1 if w.capacity_factor is None else int(math.floor(T * w.k / w.E * w.capacity_factor))
     ids = [route_by_rank(logits[t], w.k, bias)[0] for t in range(T)]
-    p = scipy.special.softmax(keys.astype(np.float64), axis=1)
+    p = scipy.special.softmax((logits if w.bias_mode == 1 else keys).astype(np.float64), axis=1)
     perm = permute_by_buckets(ids, w.E, cap)
     G = np.zeros((T, w.E))
     for t in range(T):
@@ -136,3 +139,49 @@ def test_zero_down_projection_and_zero_capacity():
     y, info = oracle.layer(x, wg, W1, W3, W2, k=2, capacity=0, shared=sh)
     assert info["n_dropped"] == w.T * w.k
     np.testing.assert_allclose(y, oracle.expert_ffn(x, *sh), rtol=0, atol=0)
+
+
+# bf16 copies of the four bf16 workloads with the same expert count, top-k, shared expert,
+# capacity factor and Zipf bias, and hidden/inner sizes cut so that the whole stacked weight
+# tensors the whole-layer entry takes stay small
+_BF16_SHRUNK = [
+    ("mixtral_prefill", dict(T=40, H=256, I=512)),
+    ("qwen3_prefill", dict(T=64, H=256, I=128)),
+    ("dsv3_decode", dict(T=48, H=256, I=128, I_shared=128)),
+    ("dsv3_decode", dict(T=48, H=256, I=128, I_shared=192)),
+    ("skewed_capacity", dict(T=512, H=256, I=128)),
+    ("skewed_capacity", dict(T=512, H=256, I=128, bias_mode=1)),
+    ("skewed_capacity", dict(T=512, H=256, I=128, bias_mode=1, renormalize=0)),
+]
+
+
+@pytest.mark.parametrize("name,kw", _BF16_SHRUNK, ids=lambda v: v if isinstance(v, str) else
+                         "-".join(f"{a}{b}" for a, b in v.items()))
+def test_whole_layer_entry_bf16_matches_dense(name, kw):
+    """oracle.layer on bf16 bit arrays (element size 2 in its row packing) against the dense
+    all-experts-then-mask reference, with the shared expert, the bias in both modes, raw
+    weights and the capacity passed through; routing and drops against brute force."""
+    import dataclasses
+    w = dataclasses.replace(moe_synth.get(name), **kw)
+    assert w.dtype == "bf16"
+    x = moe_synth.x(w)
+    assert x.dtype == np.uint16
+    W = Weights(w)
+    shared = moe_synth.shared_weights(w)
+    ref, ids, perm = _dense_reference(w, x, W, shared)
+    W1, W3, W2 = moe_synth.all_expert_weights(w)
+    cap = oracle.capacity(w.T, w.k, w.E, w.capacity_factor)
+    y, info = oracle.layer(x, moe_synth.gate_weight(w), W1, W3, W2, k=w.k, capacity=cap,
+                           renormalize=w.renormalize, bias=moe_synth.logit_bias(w),
+                           shared=shared, bias_mode=w.bias_mode)
+    assert info["ids"].tolist() == ids
+    assert info["pos"].tolist() == perm["pos"]
+    assert info["counts"].tolist() == perm["counts"]
+    assert info["n_dropped"] == perm["n_dropped"]
+    np.testing.assert_allclose(y, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+    if w.capacity_factor is not None:
+        assert info["n_dropped"] > 0   # the capacity bites
+    # the same layer from the step-wise oracle calls
+    r = routing(w, x)
+    got = layer_tokens(w, x, r, np.arange(w.T), W, shared)
+    np.testing.assert_allclose(y, got, rtol=1e-12, atol=1e-12 * np.abs(got).max())
