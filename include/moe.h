@@ -20,7 +20,11 @@
  *    `ws_bytes`), sized by moe_workspace_bytes().
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work and return; outputs are ready when the stream reaches that point.
- *    No call synchronises with the host.
+ *    No call synchronises with the host, with one exception:
+ *    moe_layer_forward_cached waits for `stream` in the middle of the call to
+ *    read the per-expert row counts back (so it cannot be captured into a HIP
+ *    graph).  The cache's bookkeeping calls (moe_cache_create, _destroy,
+ *    _slots) are host-only.
  *  - Layouts are row-major and contiguous.  Weights use the [out, in] layout
  *    of a linear layer, so both GEMM operands are contiguous along the
  *    reduction dimension.
@@ -28,8 +32,12 @@
  *    packed rows and y.  Accumulation is always fp32; logits and routing
  *    weights are always fp32; ids, counts, offsets and positions are int32.
  *  - Arguments are checked on the host before anything is launched.  On error
- *    nothing is launched and outputs are untouched.  No C++ exception crosses
- *    the ABI.  T = 0 is a valid no-op.
+ *    nothing is launched and outputs are untouched, with one exception:
+ *    moe_layer_forward_cached learns how many distinct experts a batch needs
+ *    only after its gate, route and permute have run, so it can return
+ *    MOE_ERR_UNSUPPORTED (more experts than cache slots) or a copy error after
+ *    enqueuing those steps; its outputs are then unspecified and the cache
+ *    unchanged.  No C++ exception crosses the ABI.  T = 0 is a valid no-op.
  *  - Deterministic: identical inputs give bitwise-identical outputs (no
  *    floating-point atomics; every sum has a fixed order).
  *  - Thread-safe: the library holds no mutable global state.
@@ -368,7 +376,11 @@ moe_status_t moe_cache_slots(const moe_expert_cache_t* cache, int32_t* slot_of);
  * resident (moe_cache_load on copy_stream), and the grouped GEMMs read each
  * expert's weights from its slot.  The shared expert (dims->I_shared > 0) is
  * given as in moe_layer_forward and is not cached.  The output is bit for bit
- * that of moe_layer_forward with the same weights.  info (host) may be NULL. */
+ * that of moe_layer_forward with the same weights.  info (host) may be NULL.
+ * The two exceptions to the conventions above: the host waits for `stream`
+ * mid-call, and a batch that needs more distinct experts than the cache has
+ * slots fails with MOE_ERR_UNSUPPORTED after the routing steps were enqueued
+ * (slots >= min(E, T*k) rules that out). */
 moe_status_t moe_layer_forward_cached(const moe_dims_t* dims, const void* x, const void* wg,
                                       const float* bias, moe_expert_cache_t* cache,
                                       const void* ws1, const void* ws3, const void* ws2, void* y,

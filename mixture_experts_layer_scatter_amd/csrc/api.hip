@@ -7,6 +7,7 @@
 #include <limits.h>
 #include <math.h>
 
+#include <atomic>
 #include <vector>
 
 using namespace moe;
@@ -115,11 +116,19 @@ moe_status_t check_dims(const moe_dims_t* d) {
   return MOE_OK;
 }
 
+// compute units of the current device, queried once per device
 int num_cus() {
-  int dev = 0, n = 0;
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

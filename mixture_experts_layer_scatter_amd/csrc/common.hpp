@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kSlotTile = 1024;    // routing slots handled by one permute block
 constexpr int kMaxExperts = 1024;  // routed experts the routing kernels support
+constexpr int kMaxDevices = 64;    // devices whose properties the host side caches
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;

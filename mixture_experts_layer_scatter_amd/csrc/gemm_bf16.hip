@@ -63,6 +63,7 @@
 //    fragment read takes 8 codes and widens them to bf16 in registers (every
 //    E4M3 value is exact in bf16), so the same bf16 MFMA runs; the per-row scale
 //    multiplies the fp32 accumulator in the epilogue (it factors out of the sum).
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -771,8 +772,17 @@ template <class SH, int EPI, bool GATHER, int GN, int WQ = kWBf16>
 static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStream_t s) {
   constexpr int LDS = Geo<SH, WQ>::LDS;
   auto kern = gemm_kernel<SH, EPI, GATHER, GN, WQ>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  // the dynamic LDS size is raised once per device for each instantiation
+  static std::atomic<uint64_t> lds_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+  if (!bit || !(lds_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    lds_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
   if (max_tiles <= 0) return hipSuccess;
   // workgroups per CU: as many as the LDS holds, at most 8 wavefronts per CU (12 for the MXFP4
   // tiles, whose wavefronts need few enough registers for three per SIMD)
