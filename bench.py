@@ -44,6 +44,10 @@ def main():
     ap.add_argument("--bias-mode", choices=("softmax", "select"), default="softmax",
                     help="how a workload's routing bias enters: inside the softmax, or ranking only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sub-workloads", default="qwen3_prefill,dsv3_decode,skewed_capacity",
+                    help="other workloads timed after the default one and reported under "
+                         "sub_results (empty: none)")
+    ap.add_argument("--sub-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -62,15 +66,68 @@ def main():
         copy_probe(args.copy_probe)
         return
 
+    import mixture_experts_layer_scatter_amd as moe  # noqa: F401  (fails loudly without libmoe.so)
+    import moe_synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = moe_synth.get(args.workload)
+    r = measure(w, args, args.steps, args.warmup, cache_slots=args.cache_slots)
+    out = {
+        "metric": METRIC,
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal draws, shapes of the named workload)",
+        "device": r["device"],
+        "config": r["config"],
+        "roofline": r["roofline"],
+        "layer": r["layer"],
+    }
+    # the other bf16 workloads of the metric, timed in the same run: the fine-grained prefill
+    # (MFMA-bound), the decode step (HBM-bound: the weight stream) and the skewed routing with
+    # capacity drops; each with its own dominant-kernel roofline and layer fraction
+    if args.sub_workloads and args.workload == "mixtral_prefill" and args.weights == "same":
+        subs = {}
+        for name in [n for n in args.sub_workloads.split(",") if n]:
+            torch.cuda.empty_cache()
+            sw = moe_synth.get(name)
+            sr = measure(sw, args, args.sub_steps, args.warmup)
+            subs[name] = {"config": sr["config"], "ms_per_step": sr["ms_per_step"],
+                          "tokens_per_s": sr["tokens_per_s"], "roofline": sr["roofline"],
+                          "layer_roofline_frac": sr["layer"]["roofline_frac"],
+                          "layer_bound": sr["layer"]["bound"],
+                          "layer_ms_median": sr["layer"]["ms_median"],
+                          "stage_ms": sr["layer"]["stage_ms"],
+                          "kept_rows": sr["layer"]["kept_rows"],
+                          "experts_touched": sr["layer"]["experts_touched"],
+                          "near_tie_tokens": sr["layer"]["near_tie_tokens"]}
+        out["sub_results"] = subs
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
+                                           bias_mode=0 if args.bias_mode == "softmax" else 1)
+    print(json.dumps(out), flush=True)
+
+
+def measure(w, args, steps, warmup, cache_slots=0):
+    """Time `steps` fused layer forwards of workload w (after `warmup` untimed ones) with the
+    inputs resident in HBM; returns the numbers of one JSON record."""
+    import numpy as np
+    import torch
+
     import mixture_experts_layer_scatter_amd as moe
     from mixture_experts_layer_scatter_amd import _lib
     from mixture_experts_layer_scatter_amd.hip_events import Event
-    import moe_synth
     from moe_synth.device import workload_tensors
 
-    w = moe_synth.get(args.workload)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     log(f"workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} Is={w.I_shared} {w.dtype}")
     t = workload_tensors(w, device=dev, log=log)
     cap = -1 if w.capacity_factor is None else moe.capacity(w.T, w.k, w.E, w.capacity_factor)
@@ -143,15 +200,15 @@ def main():
     else:
         near_ties, min_margin = 0, None
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region: events around the dominant kernel and around the whole layer, on the launch
     # stream (the layer's per-step spans give the median and the minimum next to the mean)
     dom = (_lib.EV_PERMUTE, _lib.EV_GATE_UP)
-    pairs = [(Event(), Event()) for _ in range(args.steps)]
-    spans = [(Event(), Event()) for _ in range(args.steps)]
+    pairs = [(Event(), Event()) for _ in range(steps)]
+    spans = [(Event(), Event()) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for (a, b), (c, e) in zip(pairs, spans):
@@ -163,7 +220,7 @@ def main():
     wall = time.perf_counter() - t0
     gu_ms = [a.elapsed_ms(b) for a, b in pairs]
     layer_ms = [c.elapsed_ms(e) for c, e in spans]
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
 
     # per-stage breakdown (untimed extra steps)
     stage = [Event() for _ in range(_lib.NUM_EVENTS)]
@@ -188,8 +245,8 @@ def main():
     load["ms"] = round(e0.elapsed_ms(e1) / n_ls, 4)
 
     cache_res = None
-    if args.cache_slots > 0 and not lowbit:
-        cache_res = measure_cache(moe, d, t, args.cache_slots, ms_per_step, log)
+    if cache_slots > 0 and not lowbit:
+        cache_res = measure_cache(moe, d, t, cache_slots, ms_per_step, log)
 
     es = 2 if w.dtype == "bf16" else 4
     # bytes of one expert weight element, and of the scales of a [rows, K] weight
@@ -220,14 +277,15 @@ def main():
     # (the timed span is the grouped GEMM plus the reduction of its split last round of tiles)
     if mx:
         shape, rows = "TileShape<32,256,1,4,2,128>", "32-row tiles"
-    elif (w.T * w.k) // w.E >= 128:
-        shape = ("TileShape<256,256,2,4,2>" if fp8
-                 else "TileShape<256,256,2,4,2,64,3>")  # 2 token-row, 3 weight LDS stages
-        rows = "256x256 tiles"
     else:
-        shape = (("TileShape<32,256,1,4,2,128>" if w.H % 128 == 0 else "TileShape<32,256,1,4,3>")
+        big = ("TileShape<256,256,2,4,2>" if fp8
+               else "TileShape<256,256,2,4,2,64,3>")  # 2 token-row, 3 weight LDS stages
+        small = (("TileShape<32,256,1,4,2,128>" if w.H % 128 == 0 else "TileShape<32,256,1,4,3>")
                  if fp8 else "TileShape<32,256,1,4,4>")
-        rows = "32-row tiles"
+        if (w.T * w.k) // w.E < 128:
+            shape, rows = small, "32-row tiles"
+        else:
+            shape, rows = big, "256x256 tiles"
     tag = ", FP8 weights" if fp8 else ", MXFP4 weights" if mx else ""
     roof["kernel"] = (f"gemm_kernel<{shape}, SwiGLU{tag}> + gemm_tail_kernel "
                       f"(grouped gate-up, {rows})")
@@ -238,43 +296,28 @@ def main():
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
               "compute_units": props.multi_processor_count, "hip": torch.version.hip}
 
-    out = {
-        "metric": METRIC,
-        "value": round(w.T / layer_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded normal draws, shapes of the named workload)",
-        "device": device,
-        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
-                   "I_shared": Is, "capacity": cap, "accumulate": "fp32",
-                   **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {}),
-                   **({"expert_weights": "fp8_e4m3_per_row_scale"} if fp8 else {}),
-                   **({"expert_weights": "mxfp4_e2m1_e8m0_per_32"} if mx else {})},
-        "roofline": roof,
-        "layer": {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
-                  "ms_median": round(float(np.median(layer_ms)), 4),
-                  "ms_min": round(float(np.min(layer_ms)), 4),
-                  "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
-                  "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
-                  "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
-                  "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
-                  "near_tie_tokens": near_ties,
-                  "min_topk_margin": None if min_margin is None else float(f"{min_margin:.3g}"),
-                  "load_stats": load,
-                  **({"lowbit_vs_bf16_weights_rel_l2": round(quant_err, 5)} if lowbit else {}),
-                  **({"expert_cache": cache_res} if cache_res is not None else {})},
-    }
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    layer_bound = ("mfma" if F / (PEAK_BF16_TFLOPS * 1e12) >= B / (PEAK_HBM_GBS * 1e9) else "hbm")
+    config = {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
+              "I_shared": Is, "capacity": cap, "accumulate": "fp32",
+              **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {}),
+              **({"expert_weights": "fp8_e4m3_per_row_scale"} if fp8 else {}),
+              **({"expert_weights": "mxfp4_e2m1_e8m0_per_32"} if mx else {})}
+    layer = {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
+             "ms_median": round(float(np.median(layer_ms)), 4),
+             "ms_min": round(float(np.min(layer_ms)), 4),
+             "gbs": round(B / layer_s / 1e9, 1), "roofline_frac": round(layer_frac, 4),
+             "bound": layer_bound,
+             "stage_ms": {n: round(float(v), 4) for n, v in zip(names, stage_ms)},
+             "kept_rows": R, "dropped": n_dropped, "experts_touched": touched,
+             "rows_per_expert_min_max": [int(cnt.min()), int(cnt.max())],
+             "near_tie_tokens": near_ties,
+             "min_topk_margin": None if min_margin is None else float(f"{min_margin:.3g}"),
+             "load_stats": load,
+             **({"lowbit_vs_bf16_weights_rel_l2": round(quant_err, 5)} if lowbit else {}),
+             **({"expert_cache": cache_res} if cache_res is not None else {})}
+    del t, ws, y
+    return {"tokens_per_s": round(w.T / layer_s, 1), "ms_per_step": round(ms_per_step, 4),
+            "device": device, "config": config, "roofline": roof, "layer": layer}
 
 
 def kernel_source_digest():
@@ -385,7 +428,7 @@ def copy_probe(nbytes):
     log(f"copy probe: 3 copies and 3 negations of {n * 4} bytes")
 
 
-def cpu_baseline(w, target_s):
+def cpu_baseline(w, target_s, bias_mode=0):
     """The oracle (plain float64 C loops) on a bounded sample of the same workload."""
     import numpy as np
 
@@ -405,7 +448,7 @@ def cpu_baseline(w, target_s):
         cap = oracle.capacity(n, w.k, w.E, w.capacity_factor)
         t0 = time.perf_counter()
         oracle.layer(xs, wg, W1, W3, W2, k=w.k, capacity=cap, renormalize=w.renormalize,
-                     bias=bias, shared=sh)
+                     bias=bias, shared=sh, bias_mode=bias_mode)
         dt = time.perf_counter() - t0
         log(f"cpu baseline: {n} tokens in {dt:.2f} s on {threads} threads")
         if dt >= target_s / 3 or n >= w.T:

@@ -59,7 +59,9 @@ Layout layout(const moe_dims_t* d) {
   // routed experts or a separate shared expert can take)
   if (d->dtype == MOE_BF16) {
     const int64_t avg = (int64_t)d->T * d->k / d->E;
-    const int big_rows = (avg >= 128 || (d->I_shared > 0 && d->T >= 128)) ? 128 : 0;
+    // a shared expert of another width runs as its own group of T rows
+    const bool own_shared = d->I_shared > 0 && d->I_shared != d->I;
+    const int big_rows = (avg >= kBigTileRows || (own_shared && d->T >= kBigTileRows)) ? kBigTileRows : 0;
     L.tail = take(gemm_tail_bytes(big_rows));
   } else {
     L.tail = take(0);

@@ -11,6 +11,8 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kSlotTile = 1024;    // routing slots handled by one permute block
 constexpr int kMaxExperts = 1024;  // routed experts the routing kernels support
 constexpr int kMaxDevices = 64;    // devices whose properties the host side caches
+// rows of a group from which its bf16 expert GEMMs take the 256 x 256 tiles
+constexpr int kBigTileRows = 128;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;

@@ -167,6 +167,14 @@ def test_layer_fp8_full_size_decode_every_token():
     check_layer_fp8(moe_synth.get("dsv3_decode"))
 
 
+def test_layer_fp8_skewed_mixed_group_sizes():
+    """FP8 weights under a skewed routing with capacity drops: experts of hundreds of rows and
+    of a handful in one launch."""
+    need_gpu()
+    check_layer_fp8(moe_synth.Workload("mixed_groups_fp8", 151, T=4096, H=512, E=16, k=2, I=256,
+                                       zipf_s=1.2, capacity_factor=1.25))
+
+
 def test_layer_fp8_shared_expert_of_another_width():
     need_gpu()
     w = moe_synth.Workload("fp8_shared_other", 200, T=100, H=256, E=16, k=4, I=128, I_shared=192)

@@ -63,6 +63,19 @@ def test_selection_only_bias_every_token(T):
     check_layer(w)
 
 
+@pytest.mark.parametrize("E,cf", [(16, 1.25), (32, None)])
+def test_skewed_mixed_group_sizes_every_token(E, cf):
+    """A Zipf-skewed routing with a bias (and a capacity) over 4096 tokens: some experts hold
+    hundreds of rows (several row tiles of the 256 x 256 tiles), others a handful (one tile with
+    most of its 32-row blocks empty), all in one persistent launch; every token checked."""
+    need_gpu()
+    w = moe_synth.Workload("mixed_groups", 150, T=4096, H=512, E=E, k=2, I=256, zipf_s=1.2,
+                           capacity_factor=cf)
+    r, rg = check_layer(w)
+    c = rg["counts"]
+    assert (c >= 256).any() and ((c > 0) & (c < 32)).any()
+
+
 def test_deterministic():
     need_gpu()
     w = moe_synth.get("qwen3_prefill").scaled(512)
