@@ -401,6 +401,34 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
                                const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ---- For callers that cannot allocate ---------------------------------------
+ * Code under HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc cannot hand the layer a workspace they allocate per call.
+ * moe_layer_forward_static is moe_layer_forward (same arguments, same kernels,
+ * bit-identical results) without the `ws` / `ws_bytes` pair: its scratch is a
+ * device array that the library owns, MOE_STATIC_SCRATCH_MIB MiB per device,
+ * allocated with the code object when the library loads on a device and held
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).
+ *  - dims whose moe_workspace_bytes() exceeds moe_static_scratch_bytes()
+ *    return MOE_ERR_WORKSPACE before anything is launched.  64 MiB holds, for
+ *    example, a decode step of 256 tokens with hidden size 7168, 256 routed
+ *    experts of width 2048, top-8, and a shared expert of width 2048.
+ *  - The array holds the last call's intermediates.  Nothing in it needs to
+ *    start at zero: every kernel writes the scratch it later reads.
+ *  - Every call on a device shares that device's array: calls that overlap on
+ *    one device (different streams, or different threads) race and give
+ *    undefined results; calls on one stream are ordered and safe.
+ * The first call on a device looks the array's address up (hipGetSymbolAddress)
+ * and keeps it; later calls only enqueue. */
+#define MOE_STATIC_SCRATCH_MIB 64
+size_t moe_static_scratch_bytes(void);
+moe_status_t moe_layer_forward_static(const moe_dims_t* dims, const void* x, const void* wg,
+                                      const float* bias, const void* w1, const void* w3,
+                                      const void* w2, const void* ws1, const void* ws3,
+                                      const void* ws2, void* y, const moe_debug_out_t* dbg,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

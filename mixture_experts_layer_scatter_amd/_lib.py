@@ -17,7 +17,7 @@ EXPORTS = ("moe_status_str", "moe_capacity", "moe_workspace_bytes", "moe_gate", 
            "moe_expert_ffn_fp8", "moe_quantize_mxfp4", "moe_expert_ffn_mxfp4",
            "moe_layer_forward_mxfp4", "moe_cache_pool_bytes", "moe_cache_create", "moe_cache_destroy",
            "moe_cache_load", "moe_cache_slots", "moe_layer_forward", "moe_layer_forward_fp8",
-           "moe_layer_forward_cached")
+           "moe_layer_forward_cached", "moe_static_scratch_bytes", "moe_layer_forward_static")
 MOE_BIAS_SOFTMAX, MOE_BIAS_SELECT = 0, 1
 
 
@@ -113,6 +113,11 @@ def lib():
         L.moe_layer_forward.restype = i32
         L.moe_layer_forward.argtypes = [D, p, p, p, p, p, p, p, p, p, p, C.POINTER(MoeDebugOut), p,
                                         sz, p]
+        L.moe_static_scratch_bytes.restype = sz
+        L.moe_static_scratch_bytes.argtypes = []
+        L.moe_layer_forward_static.restype = i32
+        L.moe_layer_forward_static.argtypes = [D, p, p, p, p, p, p, p, p, p, p,
+                                               C.POINTER(MoeDebugOut), p]
         _lib = L
     return _lib
 

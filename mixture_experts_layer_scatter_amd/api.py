@@ -381,3 +381,26 @@ def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None
         C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)), "moe_layer_forward")
     return y
+
+
+def static_scratch_bytes() -> int:
+    """Bytes of the library-owned scratch array moe_layer_forward_static uses (per device)."""
+    return int(_lib.lib().moe_static_scratch_bytes())
+
+
+def layer_forward_static(d: Dims, x, wg, bias, w1, w3, w2, y, shared=None, debug=None,
+                         stream=None):
+    """The fused layer on the library's own scratch array (no workspace, nothing allocated by
+    the call).  y must be given: this entry point is for callers that cannot allocate."""
+    dt = d.torch_dtype
+    s1 = s3 = s2 = None
+    if shared is not None:
+        s1, s3, s2 = shared
+    dbg = _debug_struct(debug) if debug else None
+    c = d.c()
+    _check(_lib.lib().moe_layer_forward_static(
+        C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),
+        _ptr(w1, dt, "w1"), _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), _ptr(s1, dt, "ws1"),
+        _ptr(s3, dt, "ws3"), _ptr(s2, dt, "ws2"), _ptr(y, dt, "y"),
+        C.byref(dbg) if dbg is not None else None, _stream(stream)), "moe_layer_forward_static")
+    return y

@@ -230,3 +230,21 @@ def test_mxfp4_entry_point_checks():
                                        None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_layer_forward_mxfp4(C.byref(_dims(dtype=L.MOE_F32)), *([p] * 16), None, p,
                                        1 << 40, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_static_scratch_entry_point_checks():
+    """moe_layer_forward_static (no workspace argument): the size of its library-owned scratch,
+    dims rejected with the same codes as moe_layer_forward, and dims whose workspace exceeds
+    the scratch rejected with MOE_ERR_WORKSPACE, all before any device call."""
+    L = _lib()
+    lib = L.lib()
+    assert lib.moe_static_scratch_bytes() == 64 << 20
+    p = C.c_void_p(16)  # never dereferenced
+    for kw, status in ((dict(k=0), L.MOE_ERR_INVALID_ARG), (dict(H=100), L.MOE_ERR_UNSUPPORTED),
+                       (dict(T=4096, H=4096, E=8, I=14336), L.MOE_ERR_WORKSPACE)):
+        d = _dims(**kw)
+        assert lib.moe_layer_forward_static(C.byref(d), p, p, None, p, p, p, None, None, None, p,
+                                            None, None) == status, kw
+    d = _dims(T=0)
+    assert lib.moe_layer_forward_static(C.byref(d), None, None, None, None, None, None, None,
+                                        None, None, None, None, None) == L.MOE_OK
