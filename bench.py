@@ -34,7 +34,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--workload", default=None,
+                    help="one workload to time (default: mixtral_prefill, followed by the "
+                         "--sub-workloads as sub-results)")
     ap.add_argument("--weights", choices=("same", "fp8", "mxfp4"), default="same",
                     help="expert weights in the layer's storage type, FP8 E4M3 with per-row "
                          "scales, or MXFP4 (quantised once before timing; bf16 layers)")
@@ -45,8 +47,8 @@ def main():
                     help="how a workload's routing bias enters: inside the softmax, or ranking only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sub-workloads", default="qwen3_prefill,dsv3_decode,skewed_capacity",
-                    help="other workloads timed after the default one and reported under "
-                         "sub_results (empty: none)")
+                    help="other workloads timed after the default one (no --workload given) and "
+                         "reported under sub_results (empty: none)")
     ap.add_argument("--sub-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -71,7 +73,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = moe_synth.get(args.workload)
+    default_run = args.workload is None
+    w = moe_synth.get(args.workload or "mixtral_prefill")
     r = measure(w, args, args.steps, args.warmup, cache_slots=args.cache_slots)
     out = {
         "metric": METRIC,
@@ -94,7 +97,7 @@ def main():
     # the other bf16 workloads of the metric, timed in the same run: the fine-grained prefill
     # (MFMA-bound), the decode step (HBM-bound: the weight stream) and the skewed routing with
     # capacity drops; each with its own dominant-kernel roofline and layer fraction
-    if args.sub_workloads and args.workload == "mixtral_prefill" and args.weights == "same":
+    if args.sub_workloads and default_run and args.weights == "same":
         subs = {}
         for name in [n for n in args.sub_workloads.split(",") if n]:
             torch.cuda.empty_cache()
