@@ -55,6 +55,12 @@ def lib():
         L.oracle_quantize_mxfp4.argtypes = [_i64, _i64, C.c_int, _p, _p, _p]
         L.oracle_dequantize_mxfp4.restype = None
         L.oracle_dequantize_mxfp4.argtypes = [_i64, _i64, _p, _p, _p]
+        L.oracle_quantize_mxfp8.restype = None
+        L.oracle_quantize_mxfp8.argtypes = [_i64, _i64, C.c_int, _p, _p, _p]
+        L.oracle_dequantize_mxfp8.restype = None
+        L.oracle_dequantize_mxfp8.argtypes = [_i64, _i64, _p, _p, _p]
+        L.oracle_expert_ffn_a8.restype = None
+        L.oracle_expert_ffn_a8.argtypes = [_i64, _i64, _i64, C.c_int, _p, C.c_int, _p, _p, _p, _p]
         L.oracle_load_stats.restype = None
         L.oracle_load_stats.argtypes = [_i64, _i64, _i64, _i32, _p, _p, _p, _p, _p]
         L.oracle_permute.restype = _i64
@@ -222,6 +228,41 @@ def dequantize_mxfp4(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     K = q.shape[-1] * 2
     out = np.empty(q.shape[:-1] + (K,), np.float64)
     lib().oracle_dequantize_mxfp4(q.size * 2 // K if K else 0, K, _ptr(q), _ptr(scales), _ptr(out))
+    return out
+
+
+def quantize_mxfp8(x: np.ndarray):
+    """MXFP8 quantisation of a [..., K] bf16-bits, float32 or float64 matrix (K % 32 == 0).
+    Returns (codes uint8 [..., K], E4M3; scales uint8 [..., K/32], E8M0)."""
+    x = _c(x)
+    K = x.shape[-1]
+    rows = x.size // K if K else 0
+    q = np.empty(x.shape, np.uint8)
+    sc = np.empty(x.shape[:-1] + (K // 32,), np.uint8)
+    lib().oracle_quantize_mxfp8(rows, K, _dt(x), _ptr(x), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def dequantize_mxfp8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.uint8)
+    K = q.shape[-1]
+    out = np.empty(q.shape, np.float64)
+    lib().oracle_dequantize_mxfp8(q.size // K if K else 0, K, _ptr(q), _ptr(scales), _ptr(out))
+    return out
+
+
+def expert_ffn_a8(xr: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """The SwiGLU FFN with MXFP8 activations (input rows and the gate-up output quantised)."""
+    xr, w1, w3, w2 = _c(xr), _c(w1), _c(w3), _c(w2)
+    M, H = xr.shape
+    I = w1.shape[0]
+    assert w1.shape == (I, H) and w3.shape == (I, H) and w2.shape == (H, I)
+    assert _dt(w1) == _dt(w3) == _dt(w2) and H % 32 == 0 and I % 32 == 0
+    out = np.empty((M, H), np.float64)
+    if M:
+        lib().oracle_expert_ffn_a8(M, H, I, _dt(xr), _ptr(xr), _dt(w1), _ptr(w1), _ptr(w3),
+                                   _ptr(w2), _ptr(out))
     return out
 
 

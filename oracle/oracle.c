@@ -143,6 +143,44 @@ void oracle_dequantize_mxfp4(int64_t rows, int64_t K, const uint8_t* q, const ui
         }
 }
 
+/* the MXFP8 rule on one block of 32 float64 values: scale code and codes */
+static uint8_t mxfp8_block(const double* v, uint8_t* q) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i)
+        if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    if (amax == 0.0) {
+        for (int i = 0; i < 32; ++i) q[i] = 0;
+        return 127;
+    }
+    int E;
+    frexp(amax, &E); /* amax = f * 2^E, f in [0.5, 1): floor(log2(amax)) = E - 1 */
+    int shared = E - 1 - 8;
+    if (shared < -126) shared = -126;
+    if (shared > 127) shared = 127;
+    for (int i = 0; i < 32; ++i) q[i] = oracle_fp8_encode((float)ldexp(v[i], -shared));
+    return (uint8_t)(shared + 127);
+}
+
+void oracle_quantize_mxfp8(int64_t rows, int64_t K, int dt, const void* x, uint8_t* q,
+                           uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / 32; ++b) {
+            double v[32];
+            for (int i = 0; i < 32; ++i) v[i] = ld(dt, x, r * K + b * 32 + i);
+            scales[r * (K / 32) + b] = mxfp8_block(v, q + r * K + b * 32);
+        }
+}
+
+void oracle_dequantize_mxfp8(int64_t rows, int64_t K, const uint8_t* q, const uint8_t* scales,
+                             double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] =
+                oracle_fp8_decode(q[r * K + k]) * ldexp(1.0, (int)scales[r * (K / 32) + k / 32] - 127);
+}
+
 void oracle_dequantize_fp8(int64_t rows, int64_t K, const uint8_t* q, const float* scales,
                            double* out) {
 #pragma omp parallel for schedule(static)
@@ -340,6 +378,42 @@ void oracle_expert_ffn(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr
             for (int64_t i = 0; i < I; ++i) s += ld(dt_w, w2, c * I + i) * h[i];
             out[m * H + c] = s;
         }
+        free(h);
+    }
+}
+
+/* quantise-dequantise n values (n % 32 == 0) through MXFP8, in place */
+static void mxfp8_round_trip(double* v, int64_t n) {
+    for (int64_t b = 0; b < n / 32; ++b) {
+        uint8_t q[32];
+        const uint8_t sc = mxfp8_block(v + b * 32, q);
+        for (int i = 0; i < 32; ++i) v[b * 32 + i] = oracle_fp8_decode(q[i]) * ldexp(1.0, (int)sc - 127);
+    }
+}
+
+void oracle_expert_ffn_a8(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr, int dt_w,
+                          const void* w1, const void* w3, const void* w2, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        double* x = (double*)malloc((size_t)H * sizeof(double));
+        double* h = (double*)malloc((size_t)I * sizeof(double));
+        for (int64_t c = 0; c < H; ++c) x[c] = ld(dt_x, xr, m * H + c);
+        mxfp8_round_trip(x, H);
+        for (int64_t i = 0; i < I; ++i) {
+            double a = 0.0, g = 0.0;
+            for (int64_t c = 0; c < H; ++c) {
+                a += ld(dt_w, w1, i * H + c) * x[c];
+                g += ld(dt_w, w3, i * H + c) * x[c];
+            }
+            h[i] = (double)(float)(silu(a) * g);
+        }
+        mxfp8_round_trip(h, I);
+        for (int64_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int64_t i = 0; i < I; ++i) s += ld(dt_w, w2, c * I + i) * h[i];
+            out[m * H + c] = s;
+        }
+        free(x);
         free(h);
     }
 }

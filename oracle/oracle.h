@@ -82,6 +82,21 @@ void oracle_quantize_mxfp4(int64_t rows, int64_t K, int dt, const void* w, uint8
 void oracle_dequantize_mxfp4(int64_t rows, int64_t K, const uint8_t* q, const uint8_t* scales,
                              double* out);
 
+/* MXFP8 activation quantisation (the OCP microscaling format with E4M3 elements: blocks of 32
+ * consecutive elements along K share one E8M0 scale 2^(s - 127)), a reading of the FP8
+ * activations of [P3] §5.2's "w4afp8" serving configuration.  Per block: amax = max |x|; if
+ * amax == 0 the scale code is 127 (scale 1) and every code 0; else e = floor(log2(amax)),
+ * shared = clamp(e - 8, -126, 127) (8 = the largest exponent of E4M3, the format's rule;
+ * block values in [448, 512) x 2^shared saturate), scale code = shared + 127, and
+ * q = fp8_encode(x / 2^shared) (exact division).  K % 32 == 0.  q [rows, K] one code per
+ * byte, row-major; scales [rows, K/32]. */
+void oracle_quantize_mxfp8(int64_t rows, int64_t K, int dt, const void* x, uint8_t* q,
+                           uint8_t* scales);
+
+/* out[r,k] = fp8_decode(q[r,k]) * 2^(scales[r, k/32] - 127), exact in float64. */
+void oracle_dequantize_mxfp8(int64_t rows, int64_t K, const uint8_t* q, const uint8_t* scales,
+                             double* out);
+
 /* Expert capacity, [P3] §2.1 (router sketch, capacity = tokens / experts x
  * factor), with the top-k factor included: floor(T*k/E*factor) in double. */
 int32_t oracle_capacity(int32_t T, int32_t k, int32_t E, double factor);
@@ -152,6 +167,13 @@ int64_t oracle_permute(int64_t T, int64_t E, int64_t k, int32_t capacity, const 
  * out [M,H] float64. */
 void oracle_expert_ffn(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr, int dt_w,
                        const void* w1, const void* w3, const void* w2, double* out);
+
+/* The SwiGLU FFN with MXFP8 activations (the "afp8" half of [P3] §5.2's w4afp8): each input
+ * row is quantised to MXFP8 along H and dequantised (x'); the gate-up output
+ * h = silu(W1 x') * (W3 x') (float64) is rounded once to fp32, quantised to MXFP8 along I and
+ * dequantised (h'); out = W2 h'.  Arguments as oracle_expert_ffn; H % 32 == 0, I % 32 == 0. */
+void oracle_expert_ffn_a8(int64_t M, int64_t H, int64_t I, int dt_x, const void* xr, int dt_w,
+                          const void* w1, const void* w3, const void* w2, double* out);
 
 /* Weighted combine and restore of token order, [P1] §2 (y = sum of g_i E_i(x))
  * and §7 (outputs return to their tokens, weighted by the router).
