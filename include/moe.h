@@ -318,6 +318,54 @@ moe_status_t moe_layer_forward_mxfp4(const moe_dims_t* dims, const void* x, cons
                                      const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
                                      void* stream);
 
+/* ---- MXFP8 activations with MXFP4 weights ---------------------------------
+ * [P3] §5.2 serves the experts with 4-bit weights and FP8 activations.
+ * Reading: the activations use the OCP microscaling MXFP8 format (E4M3
+ * elements with one E8M0 scale per 32 consecutive elements of a row), the
+ * weights MXFP4 as moe_quantize_mxfp4 writes them, and the products run on
+ * CDNA4's block-scaled MFMA, which applies both scales in hardware.  Each
+ * expert FFN quantises twice: its input rows (along H) and its SwiGLU
+ * activation (along I, after silu(a) * g is formed in fp32). */
+
+/* MXFP8 quantisation: x [rows, K] of storage `dtype` (MOE_BF16 or MOE_F32),
+ * K % 32 == 0 and K > 0 (else MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED).
+ * Per block of 32: amax = max |x|; 0 gives scale code 127 and codes 0; else
+ * shared = clamp(floor(log2(amax)) - 8, -126, 127) (8: the largest E4M3
+ * exponent), scale code = shared + 127, and each code the E4M3 value nearest
+ * to x / 2^shared (ties to even, saturating at +-448).
+ *  q [rows, K] u8 codes and scales [rows, K/32] u8, both row-major device
+ *  outputs; the dequantised value is value(q) * 2^(scale - 127). */
+moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t K, int32_t dtype, const void* x,
+                                uint8_t* q, uint8_t* scales, void* stream);
+
+/* moe_expert_ffn_mxfp4 with MXFP8 activations: x_packed (bf16) is quantised
+ * to MXFP8 inside the call, then
+ *  y_packed[r] = W2' Q( silu(W1' Q(x_packed[r])) * (W3' Q(x_packed[r])) )
+ * with Q the MXFP8 round trip along the row and W' the dequantised MXFP4
+ * weights; every product is exact and sums in fp32.  dims->dtype must be
+ * MOE_BF16; H and I multiples of 128.  Every group size runs on the 32-row
+ * tiles.  The workspace (moe_workspace_bytes) holds the quantised rows. */
+moe_status_t moe_expert_ffn_w4a8(const moe_dims_t* dims, const void* x_packed,
+                                 const int32_t* offsets, const uint8_t* w1q, const uint8_t* w1s,
+                                 const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                 const uint8_t* w2s, void* y_packed, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* moe_layer_forward_mxfp4 with MXFP8 activations: the gate and the routing
+ * run on the bf16 x as in moe_layer_forward; x is quantised to MXFP8 once per
+ * token (the expert GEMMs gather its rows), and every expert, the shared one
+ * included, computes as moe_expert_ffn_w4a8.  Same arguments and limits as
+ * moe_layer_forward_mxfp4.  With debug events, the quantisation of x is timed
+ * with the permute step. */
+moe_status_t moe_layer_forward_w4a8(const moe_dims_t* dims, const void* x, const void* wg,
+                                    const float* bias, const uint8_t* w1q, const uint8_t* w1s,
+                                    const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                    const uint8_t* w2s, const uint8_t* ws1q, const uint8_t* ws1s,
+                                    const uint8_t* ws3q, const uint8_t* ws3s,
+                                    const uint8_t* ws2q, const uint8_t* ws2s, void* y,
+                                    const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* ---- Expert cache: experts resident in HBM up to a number of slots ----------
  * [P3] §3.2 keeps a subset of the experts in HBM and loads the others from
  * host memory before a batch needs them, evicting the least recently used

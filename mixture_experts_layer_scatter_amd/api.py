@@ -199,22 +199,56 @@ def quantize_mxfp4(w, q=None, scales=None, stream=None):
     return q, scales
 
 
-def expert_ffn_mxfp4(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None):
+def quantize_mxfp8(x, q=None, scales=None, stream=None):
+    """MXFP8 quantisation of a bf16 or fp32 device tensor [..., K] (K % 32 == 0).  Returns
+    (E4M3 codes uint8 of x's shape, E8M0 scales uint8 [..., K/32]), both row-major."""
+    dt = {torch.bfloat16: _lib.MOE_BF16, torch.float32: _lib.MOE_F32}.get(x.dtype)
+    if dt is None:
+        raise TypeError(f"quantize_mxfp8: bf16 or fp32 input, got {x.dtype}")
+    K = x.shape[-1]
+    rows = x.numel() // K if K else 0
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (K // 32,), dtype=torch.uint8, device=x.device)
+    _check(_lib.lib().moe_quantize_mxfp8(rows, K, dt, _ptr(x, None, "x"), _ptr(q, torch.uint8, "q"),
+                                         _ptr(scales, torch.uint8, "scales"), _stream(stream)),
+           "moe_quantize_mxfp8")
+    return q, scales
+
+
+def expert_ffn_mxfp4(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None,
+                     _entry="moe_expert_ffn_mxfp4"):
     """moe_expert_ffn_mxfp4; w1, w3, w2 are (codes, scales) pairs from quantize_mxfp4."""
     c = d.c()
     dt = d.torch_dtype
     (q1, s1), (q3, s3), (q2, s2) = w1, w3, w2
     u8 = torch.uint8
-    _check(_lib.lib().moe_expert_ffn_mxfp4(
+    _check(getattr(_lib.lib(), _entry)(
         C.byref(c), _ptr(x_packed, dt, "x_packed"), _ptr(offsets, torch.int32, "offsets"),
         _ptr(q1, u8, "w1q"), _ptr(s1, u8, "w1s"), _ptr(q3, u8, "w3q"), _ptr(s3, u8, "w3s"),
         _ptr(q2, u8, "w2q"), _ptr(s2, u8, "w2s"), _ptr(y_packed, dt, "y_packed"),
         _ptr(ws, torch.uint8, "ws"), 0 if ws is None else ws.numel(), _stream(stream)),
-        "moe_expert_ffn_mxfp4")
+        _entry)
+
+
+def expert_ffn_w4a8(d: Dims, x_packed, offsets, w1, w3, w2, y_packed, ws, stream=None):
+    """moe_expert_ffn_w4a8: MXFP4 weights ((codes, scales) pairs from quantize_mxfp4) on
+    MXFP8 activations (x_packed is bf16; the call quantises it)."""
+    expert_ffn_mxfp4(d, x_packed, offsets, w1, w3, w2, y_packed, ws, stream,
+                     _entry="moe_expert_ffn_w4a8")
+
+
+def layer_forward_w4a8(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None,
+                       debug=None, stream=None):
+    """The fused layer with MXFP4 expert weights on MXFP8 activations (arguments as
+    layer_forward_mxfp4).  Returns y."""
+    return layer_forward_mxfp4(d, x, wg, bias, w1, w3, w2, shared, y, ws, debug, stream,
+                               _entry="moe_layer_forward_w4a8")
 
 
 def layer_forward_mxfp4(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None,
-                        debug=None, stream=None):
+                        debug=None, stream=None, _entry="moe_layer_forward_mxfp4"):
     """The fused layer with MXFP4 expert weights ((codes, scales) pairs from quantize_mxfp4,
     the shared expert's in `shared`).  Returns y."""
     dt = d.torch_dtype
@@ -228,13 +262,13 @@ def layer_forward_mxfp4(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, w
     (e1, t1), (e3, t3), (e2, t2) = shared if shared is not None else (none, none, none)
     dbg = _debug_struct(debug) if debug else None
     c = d.c()
-    _check(_lib.lib().moe_layer_forward_mxfp4(
+    _check(getattr(_lib.lib(), _entry)(
         C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),
         _ptr(q1, u8, "w1q"), _ptr(s1, u8, "w1s"), _ptr(q3, u8, "w3q"), _ptr(s3, u8, "w3s"),
         _ptr(q2, u8, "w2q"), _ptr(s2, u8, "w2s"), _ptr(e1, u8, "ws1q"), _ptr(t1, u8, "ws1s"),
         _ptr(e3, u8, "ws3q"), _ptr(t3, u8, "ws3s"), _ptr(e2, u8, "ws2q"), _ptr(t2, u8, "ws2s"),
         _ptr(y, dt, "y"), C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"),
-        ws.numel(), _stream(stream)), "moe_layer_forward_mxfp4")
+        ws.numel(), _stream(stream)), _entry)
     return y
 
 

@@ -21,8 +21,11 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Byte layout of the workspace; one layout serves every call.
 struct Layout {
   size_t tail, gate_part, logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn, pos,
-      dropped, row_token, act, yp, yps, total;
+      dropped, row_token, xq, act, yp, yps, total;
 };
+
+// bytes of `rows` MXFP8 rows of K codes: the codes, then (256-byte aligned) their E8M0 scales
+size_t mx8_bytes(size_t rows, size_t K) { return align_up(rows * K) + rows * (K / 32); }
 
 int elem_bytes(const moe_dims_t* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 
@@ -82,8 +85,17 @@ Layout layout(const moe_dims_t* d) {
   L.pos = take(n * 4);
   L.dropped = take(n);
   L.row_token = take((n + T) * 4);
-  L.act = take(((rows > T ? rows : T)) * imax * es);
-  L.yp = take(rows * (size_t)d->H * es);
+  // the layer's input rows in MXFP8 (layers with MXFP8 activations; bf16 layers only)
+  const bool mx8 = d->dtype == MOE_BF16 && d->H % 32 == 0;
+  L.xq = take(mx8 ? mx8_bytes(T, d->H) : 0);
+  // the gate-up output: bf16 rows, or MXFP8 rows with their scales
+  const size_t act_rows = rows > T ? rows : T;
+  const size_t act_bytes = act_rows * imax * es;
+  L.act = take(mx8 && mx8_bytes(act_rows, imax) > act_bytes ? mx8_bytes(act_rows, imax) : act_bytes);
+  // packed expert outputs; the expert FFN call with MXFP8 activations quantises its packed input
+  // rows here first
+  const size_t yp_bytes = rows * (size_t)d->H * es;
+  L.yp = take(mx8 && mx8_bytes(n, d->H) > yp_bytes ? mx8_bytes(n, d->H) : yp_bytes);
   L.yps = take(d->I_shared > 0 && !fold ? T * (size_t)d->H * es : 0);
   L.total = o;
   return L;
@@ -202,13 +214,14 @@ struct ExpertWeights {
   const void *w1, *w3, *w2;
   const float *s1, *s3, *s2;      // FP8 E4M3: per-row scales
   const uint8_t *m1, *m3, *m2;    // MXFP4: E8M0 scales per 32 k
+  bool a8 = false;                // MXFP4 weights applied to MXFP8 activations
   bool fp8() const { return s1 != nullptr; }
   bool mx() const { return m1 != nullptr; }
-  int fmt() const { return fp8() ? 1 : mx() ? 2 : 0; }
+  int fmt() const { return fp8() ? 1 : mx() ? (a8 ? 3 : 2) : 0; }
   bool complete() const {
     const bool s = s1 && s3 && s2, no_s = !s1 && !s3 && !s2;
     const bool m = m1 && m3 && m2, no_m = !m1 && !m3 && !m2;
-    return w1 && w3 && w2 && (s || no_s) && (m || no_m) && !(s && m);
+    return w1 && w3 && w2 && (s || no_s) && (m || no_m) && !(s && m) && (!a8 || m);
   }
 };
 
@@ -223,10 +236,17 @@ ExpertWeights mxfp4_weights(const void* w1, const uint8_t* s1, const void* w3, c
                             const void* w2, const uint8_t* s2) {
   return ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr, s1, s3, s2};
 }
+ExpertWeights w4a8_weights(const void* w1, const uint8_t* s1, const void* w3, const uint8_t* s3,
+                           const void* w2, const uint8_t* s2) {
+  return ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr, s1, s3, s2, true};
+}
 
 // grouped gate-up + down over G groups whose packed row ranges are offsets[0..G]; groups past
-// G_routed (at most one) take the extra weights X
-hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row_map,
+// G_routed (at most one) take the extra weights X.  With W.a8, `a` holds MXFP8 codes and a_mx
+// their scales, and the activation goes through `act` in MXFP8 (codes, then the scales at
+// align_up(max_rows * I)).
+hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const uint8_t* a_mx,
+                   const int32_t* row_map,
                    int64_t a_rows, int64_t max_rows, const int32_t* offsets, int G, int G_routed,
                    const ExpertWeights& W, const ExpertWeights* X, void* act, void* out,
                    int32_t* ts_gu, int32_t* ts_dn, int avg_rows, float* tail, hipStream_t s,
@@ -236,6 +256,8 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   if (G_routed < 0 || G_routed > G || !W.complete() || (W.fmt() && !bf16)) return hipErrorInvalidValue;
   if (G > G_routed && (!X || !X->complete() || X->fmt() != W.fmt())) return hipErrorInvalidValue;
   if (W.mx()) avg_rows = 0;  // MXFP4 runs on the 32-row tiles for every group size
+  if (W.a8 != (a_mx != nullptr)) return hipErrorInvalidValue;
+  uint8_t* act_mx = W.a8 ? (uint8_t*)act + align_up((size_t)max_rows * I) : nullptr;
   if (group_slot && !bf16) return hipErrorInvalidValue;  // slot indirection: MFMA path only
   int bm_gu, nt_gu, bm_dn, nt_dn;
   if (bf16) {
@@ -251,6 +273,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
 
   GroupedGemm gu = {};
   gu.a = a;
+  gu.a_mx = a_mx;
   gu.row_map = row_map;
   gu.a_rows = a_rows;
   gu.max_rows = max_rows;
@@ -273,6 +296,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
   gu.K = d->H;
   gu.c = act;
   gu.ldc = I;
+  gu.c_mx = act_mx;
   gu.offsets = offsets;
   gu.G = G;
   gu.G_routed = G_routed;
@@ -282,6 +306,7 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const int32_t* row
 
   GroupedGemm dn = {};
   dn.a = act;
+  dn.a_mx = act_mx;
   dn.a_rows = max_rows;
   dn.max_rows = max_rows;
   dn.b = W.w2;
@@ -445,9 +470,18 @@ moe_status_t expert_ffn_impl(const moe_dims_t* d, const void* x_packed, const in
   if (d->T == 0) return MOE_OK;
   const int64_t n = (int64_t)d->T * d->k;
   const int avg = (int)(n / d->E);
-  MOE_TRY(run_ffn(d, d->I, x_packed, nullptr, n, n, offsets, d->E, d->E, W, nullptr,
+  hipStream_t s = (hipStream_t)stream;
+  const void* a = x_packed;
+  const uint8_t* a_mx = nullptr;
+  if (W.a8) {  // the packed rows in MXFP8, in the packed-output area (unused by this call)
+    uint8_t* xq = at<uint8_t>(ws, L.yp);
+    a_mx = xq + align_up((size_t)n * d->H);
+    MOE_TRY(launch_quantize_mxfp8(x_packed, 1, n, d->H, xq, (uint8_t*)a_mx, s));
+    a = xq;
+  }
+  MOE_TRY(run_ffn(d, d->I, a, a_mx, nullptr, n, n, offsets, d->E, d->E, W, nullptr,
                   at<void>(ws, L.act), y_packed, at<int32_t>(ws, L.ts_gu),
-                  at<int32_t>(ws, L.ts_dn), avg, at<float>(ws, L.tail), (hipStream_t)stream));
+                  at<int32_t>(ws, L.ts_dn), avg, at<float>(ws, L.tail), s));
   return MOE_OK;
 }
 
@@ -493,6 +527,26 @@ moe_status_t moe_expert_ffn_mxfp4(const moe_dims_t* d, const void* x_packed,
   if (!w1s || !w3s || !w2s) return MOE_ERR_INVALID_ARG;
   return expert_ffn_impl(d, x_packed, offsets,
                          mxfp4_weights(w1q, w1s, w3q, w3s, w2q, w2s),
+                         y_packed, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t K, int32_t dtype, const void* x,
+                                uint8_t* q, uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || (dtype != MOE_BF16 && dtype != MOE_F32)) return MOE_ERR_INVALID_ARG;
+  if (K % 32) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_quantize_mxfp8(x, dtype == MOE_BF16, rows, K, q, scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_w4a8(const moe_dims_t* d, const void* x_packed,
+                                 const int32_t* offsets, const uint8_t* w1q, const uint8_t* w1s,
+                                 const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                 const uint8_t* w2s, void* y_packed, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!w1s || !w3s || !w2s) return MOE_ERR_INVALID_ARG;
+  return expert_ffn_impl(d, x_packed, offsets, w4a8_weights(w1q, w1s, w3q, w3s, w2q, w2s),
                          y_packed, ws, ws_bytes, stream);
 }
 
@@ -598,7 +652,16 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
   const int64_t max_rows = (int64_t)n + (fold ? T : 0);
   const int avg = n / E;
   void* yp = at<void>(ws, L.yp);
-  MOE_TRY(run_ffn(d, d->I, x, row_token, T, max_rows, offsets, G, E, W, fold ? &SW : nullptr,
+  // MXFP8 activations: the token rows are quantised once, and the expert GEMMs gather them
+  const void* xa = x;
+  const uint8_t* xa_mx = nullptr;
+  if (W.a8) {
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    xa_mx = xq + align_up((size_t)T * d->H);
+    MOE_TRY(launch_quantize_mxfp8(x, 1, T, d->H, xq, (uint8_t*)xa_mx, s));
+    xa = xq;
+  }
+  MOE_TRY(run_ffn(d, d->I, xa, xa_mx, row_token, T, max_rows, offsets, G, E, W, fold ? &SW : nullptr,
                   at<void>(ws, L.act), yp, at<int32_t>(ws, L.ts_gu), at<int32_t>(ws, L.ts_dn), avg,
                   at<float>(ws, L.tail), s, ev, group_slot));
   const void* ys = nullptr;
@@ -613,7 +676,7 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
     int32_t* off2 = at<int32_t>(ws, L.raw);  // two ints: [0, T]
     whole_range_kernel<<<1, 1, 0, s>>>(off2, T);
     MOE_TRY(hipGetLastError());
-    MOE_TRY(run_ffn(d, d->I_shared, x, nullptr, T, T, off2, 1, 1, SW, nullptr,
+    MOE_TRY(run_ffn(d, d->I_shared, xa, xa_mx, nullptr, T, T, off2, 1, 1, SW, nullptr,
                     at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
                     at<int32_t>(ws, L.ts_dn), T, at<float>(ws, L.tail), s));
     ys = at<void>(ws, L.yps);
@@ -681,6 +744,22 @@ moe_status_t moe_layer_forward_mxfp4(const moe_dims_t* d, const void* x, const v
   return layer_forward_impl(
       d, x, wg, bias, mxfp4_weights(w1q, w1s, w3q, w3s, w2q, w2s),
       mxfp4_weights(ws1q, ws1s, ws3q, ws3s, ws2q, ws2s), y, dbg, ws,
+      ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_w4a8(const moe_dims_t* d, const void* x, const void* wg,
+                                    const float* bias, const uint8_t* w1q, const uint8_t* w1s,
+                                    const uint8_t* w3q, const uint8_t* w3s, const uint8_t* w2q,
+                                    const uint8_t* w2s, const uint8_t* ws1q, const uint8_t* ws1s,
+                                    const uint8_t* ws3q, const uint8_t* ws3s,
+                                    const uint8_t* ws2q, const uint8_t* ws2s, void* y,
+                                    const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (d && d->T > 0 && (!w1s || !w3s || !w2s)) return MOE_ERR_INVALID_ARG;
+  if (d && d->I_shared > 0 && (!ws1s || !ws3s || !ws2s)) return MOE_ERR_INVALID_ARG;
+  return layer_forward_impl(
+      d, x, wg, bias, w4a8_weights(w1q, w1s, w3q, w3s, w2q, w2s),
+      w4a8_weights(ws1q, ws1s, ws3q, ws3s, ws2q, ws2s), y, dbg, ws,
       ws_bytes, stream);
 }
 

@@ -30,6 +30,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// MXFP8 (the OCP microscaling format with E4M3 elements and one E8M0 scale per 32 elements):
+// the scale code of a block whose largest magnitude is amax: 2^(floor(log2 amax) - 8), the
+// exponent clamped to [-126, 127] so that the scale is a normal float; 127 (scale 1) for a
+// zero block.
+__device__ __forceinline__ uint32_t mxfp8_scale_code(float amax) {
+  if (!(amax > 0.f)) return 127u;
+  // amax = m * 2^e with m in [0.5, 1): floor(log2(amax)) = e - 1
+  int shared = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+  shared = shared < -126 ? -126 : (shared > 127 ? 127 : shared);
+  return (uint32_t)(shared + 127);
+}
+
+// four values of a block with scale code sc -> four E4M3 codes in one dword (value 0 in the low
+// byte).  The hardware conversion divides by the scale and rounds to nearest even, but turns
+// quotients above the largest finite E4M3 value into NaN, so the values are first clamped to
+// +-448 times the scale.
+__device__ __forceinline__ uint32_t mxfp8_pack4(float a, float b, float c, float d, uint32_t sc) {
+  typedef __attribute__((__vector_size__(2 * sizeof(short)))) short short2_t;
+  const float scale = __uint_as_float(sc << 23), lim = 448.f * scale;
+  a = fminf(fmaxf(a, -lim), lim);
+  b = fminf(fmaxf(b, -lim), lim);
+  c = fminf(fmaxf(c, -lim), lim);
+  d = fminf(fmaxf(d, -lim), lim);
+  short2_t r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -80,12 +109,16 @@ hipError_t launch_combine(const void* yp, const int32_t* pos, const float* w, co
                           hipStream_t s);
 
 // gemm_bf16.hip / gemm_f32.hip: grouped GEMMs
-enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
+// EPI_SWIGLU_MX8: the SwiGLU output quantised to MXFP8 (codes in c, E8M0 scales in c_mx)
+enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_SWIGLU_MX8 = 3 };
 
 struct GroupedGemm {
   // A: packed rows [*, K]; row r of group g reads A row (row_map ? row_map[r] : r)
   const void* a;
   const int32_t* row_map;
+  // MXFP8 activations (with MXFP4 weights only): a holds E4M3 codes [a_rows, K] and a_mx the
+  // E8M0 scales [a_rows, K/32], both row-major.  Null a_mx: a holds bf16 (or fp32) rows.
+  const uint8_t* a_mx;
   int64_t a_rows;            // rows addressable in a (for range checks)
   int64_t max_rows;          // upper bound of the packed rows over all groups
   // B: per group [N_b, K] with N_b = N (or 2 panels of N for SwiGLU: b and b2)
@@ -115,6 +148,7 @@ struct GroupedGemm {
   // output C [*, ldc]
   void* c;
   int ldc;
+  uint8_t* c_mx;             // EPI_SWIGLU_MX8: E8M0 scales [*, N/32] of the MXFP8 output
   // groups
   const int32_t* offsets;    // [G+1] packed row range of each group (device) or null
   int G;                     // groups (routed + extra)
@@ -157,6 +191,10 @@ hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uin
                                float* scales, hipStream_t s);
 // MXFP4 quantisation (K % 32 == 0): codes [rows, K/2], E8M0 scales [rows, K/32]
 hipError_t launch_quantize_mxfp4(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
+                                 uint8_t* scales, hipStream_t s);
+// MXFP8 quantisation of activations (K % 32 == 0): codes [rows, K] and E8M0 scales
+// [rows, K/32], both row-major
+hipError_t launch_quantize_mxfp8(const void* x, int bf16, int64_t rows, int K, uint8_t* q,
                                  uint8_t* scales, hipStream_t s);
 
 // out[i] = sum_s part[s * n + i] (fixed order)

@@ -71,6 +71,8 @@
 namespace moe {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -164,16 +166,17 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
   return r.h;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_ = 64, int SB_ = S_>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_ = 64, int SB_ = S_, int AE_ = 2>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int AE = AE_;  // bytes of an A (token-row) element: 2 (bf16), 1 (MXFP8)
   // LDS stages of the weight operand (S: of the token rows).  With 256 x 256 tiles two full
   // stages take 128 KB of the 160 KB, so one operand can get a third slot: a step more of
   // latency for its L2 misses
   static constexpr int SB = SB_;
   static_assert(SB == S || (S == 2 && SB == 3) || (S == 3 && SB == 2), "stage counts");
   static constexpr int BK = BK_;                      // k elements per LDS stage
-  static constexpr int ROWB = BK * 2, CH = ROWB / 16; // bytes and 16-byte chunks of an A row
+  static constexpr int ROWB = BK * AE, CH = ROWB / 16; // bytes and 16-byte chunks of an A row
   static constexpr int WAVES = WM * WN, THREADS = WAVES * kWave;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wavefront tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32 x 32 MFMA blocks per wavefront
@@ -182,31 +185,51 @@ struct TileShape {
   static constexpr int A_LOADS = BM / RPL / WAVES;
   static constexpr int A_BYTES = BM * ROWB;
   static_assert(BK == 64 || BK == 128, "k-step");
+  static_assert(AE == 2 || (AE == 1 && BK == 128), "MXFP8 rows: 128 codes (one line) per stage");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wavefront tile is a multiple of 32 x 32");
   static_assert(A_LOADS * RPL * WAVES == BM, "load split");
 };
 
+// epilogues that pair W1 and W3 blocks (silu(W1 x) * W3 x)
+__host__ __device__ constexpr bool is_swiglu(int epi) {
+  return epi == EPI_SWIGLU || epi == EPI_SWIGLU_MX8;
+}
+
 // weight storage of the grouped GEMM's second operand
-constexpr int kWBf16 = 0, kWFp8 = 1, kWMxfp4 = 2;
+// kWMx4A8: MXFP4 weights with MXFP8 token rows (the scaled f8f6f4 MFMA)
+constexpr int kWBf16 = 0, kWFp8 = 1, kWMxfp4 = 2, kWMx4A8 = 3;
 
 // LDS geometry of a shape with bf16, E4M3 or MXFP4 weights
 template <class SH, int WQ>
 struct Geo {
+  static constexpr bool MX4 = WQ == kWMxfp4 || WQ == kWMx4A8;  // E2M1 weights, E8M0 scales
+  static constexpr bool A8 = WQ == kWMx4A8;                      // E4M3 token rows
+  static_assert(A8 == (SH::AE == 1), "MXFP8 token rows go with the 1-byte tile shapes");
   static constexpr int B_ROWB = WQ == kWBf16 ? SH::ROWB : WQ == kWFp8 ? SH::BK : SH::BK / 2;
   static constexpr int B_CH = B_ROWB / 16;            // its 16-byte chunks
   static constexpr int B_RPL = 1024 / B_ROWB;         // weight rows one 1 KB load covers
   static constexpr int B_LOADS = SH::BN / B_RPL / SH::WAVES;
   // MXFP4: the stage's E8M0 scales, one dword (BK / 32 = 4 blocks) per weight row, loaded 32
   // rows per wavefront load into 256-byte areas (the other 32 lanes carry no address)
-  static constexpr int SC_LOADS = WQ == kWMxfp4 ? SH::BN / 32 / SH::WAVES : 0;
-  static constexpr int SC_BYTES = WQ == kWMxfp4 ? SH::BN / 32 * 256 : 0;
+  static constexpr int SC_LOADS = MX4 ? SH::BN / 32 / SH::WAVES : 0;
+  static constexpr int SC_BYTES = MX4 ? SH::BN / 32 * 256 : 0;
+  // MXFP8 token rows: the stage's E8M0 scales, one dword (BK / 32 = 4 blocks) per row, 32 rows
+  // per load into 256-byte areas; every wavefront issues the same count (areas past the tile's
+  // rows take zeros), so the wait counts stay uniform
+  static constexpr int A_SC_LOADS = A8 ? (SH::BM / 32 + SH::WAVES - 1) / SH::WAVES : 0;
+  static constexpr int A_SC_BYTES = A_SC_LOADS * SH::WAVES * 256;
+  static constexpr int LA = SH::A_LOADS + A_SC_LOADS;    // token-row loads per wavefront
   static constexpr int LB = B_LOADS + SC_LOADS;          // weight-side loads per wavefront
-  static constexpr int L = SH::A_LOADS + LB;             // loads per wavefront per stage
+  static constexpr int L = LA + LB;                      // loads per wavefront per stage
+  static constexpr int A_STAGE = SH::A_BYTES + A_SC_BYTES;
   static constexpr int B_STAGE = SH::BN * B_ROWB + SC_BYTES;
-  static_assert(WQ != kWMxfp4 || (SH::BK == 128 && SC_LOADS * 32 * SH::WAVES == SH::BN),
+  static_assert(!MX4 || (SH::BK == 128 && SC_LOADS * 32 * SH::WAVES == SH::BN),
                 "MXFP4 stages hold 128 k: one scale dword per row");
+  static_assert(!A8 || A_SC_LOADS * 32 * SH::WAVES >= SH::BM, "MXFP8 scale loads");
+  // MFMA sub-steps per stage: 16 k (bf16 32x32x16) or 64 k (scaled f8f6f4 32x32x64)
+  static constexpr int KSUB = A8 ? SH::BK / 64 : SH::KK;
   // LDS: S slots of the token-row tile, then SB slots of the weight tile
-  static constexpr int LDS = SH::S * SH::A_BYTES + SH::SB * B_STAGE;
+  static constexpr int LDS = SH::S * A_STAGE + SH::SB * B_STAGE;
   static_assert(B_LOADS * B_RPL * SH::WAVES == SH::BN, "load split");
   // Each barrier issues the operand with fewer stages first (its step is needed sooner).  WAIT:
   // the loads a wavefront issued after the token rows and weights of step lk + 1, when step lk
@@ -214,7 +237,7 @@ struct Geo {
   // at the start of a tile; the previous tile's stores were issued after the prologue, so with
   // S != SB it waits for everything rather than count on loads and stores completing in order.
   static constexpr int WAIT = SH::S == SH::SB ? (SH::S - 2) * L
-                              : SH::S < SH::SB ? LB : SH::A_LOADS;
+                              : SH::S < SH::SB ? LB : LA;
   static constexpr int PRO_WAIT = SH::S == SH::SB ? (SH::S - 2) * L : 0;
   static_assert(SH::S >= 2 && WAIT < 64 && PRO_WAIT < 64, "loads in flight fit the vmcnt counter");
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -237,6 +260,9 @@ using DecodeShapeFp8K128 = TileShape<32, 256, 1, 4, 2, 128>;
 // decode layer 1.26 -> 1.19 ms against three stages and two workgroups); every group size runs
 // on this 32-row shape
 using ShapeMxfp4 = TileShape<32, 256, 1, 4, 2, 128>;
+// MXFP8 token rows with MXFP4 weights: the same 32-row blocking and two stages; a stage's token
+// rows are one 128-byte line each (128 E4M3 codes) plus a scale dword (46 KB for both stages)
+using ShapeMx4A8 = TileShape<32, 256, 1, 4, 2, 128, 2, 1>;
 
 // ---- tile bookkeeping shared by the GEMM and its tail reduction ---------------------------------
 
@@ -327,17 +353,17 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
   if constexpr (WQ == kWFp8) {
     const bool extra = p.tile_start && t.g >= p.G_routed;
     const float* s1 = extra ? p.b_scale_extra : p.b_scale + (int64_t)t.w * p.N;
-    const float* s2 = EPI != EPI_SWIGLU ? s1
+    const float* s2 = !is_swiglu(EPI) ? s1
                       : extra ? p.b2_scale_extra : p.b2_scale + (int64_t)t.w * p.N;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // SwiGLU: blocks j (W1) and j + 1 (W3) hold the same 32 columns
-        const int col = EPI == EPI_SWIGLU
+        const int col = is_swiglu(EPI)
                             ? t.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32 + 8 * q + 4 * hi
                             : t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
-        const float* src = (EPI == EPI_SWIGLU && (j & 1)) ? s2 : s1;
+        const float* src = (is_swiglu(EPI) && (j & 1)) ? s2 : s1;
         sc[j][q] = col < p.N ? *(const float4*)(src + col) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
   }
@@ -373,6 +399,32 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
             *(uint2*)(crow + col) = v;
           }
         }
+    } else if constexpr (EPI == EPI_SWIGLU_MX8) {
+      // MXFP8 output: a 32-column block of the activation row is one MX block, held half by
+      // this lane and half by lane ^ 32 (the same token row), which share its largest magnitude
+      uint8_t* crow = (uint8_t*)p.c + (out_row0 + tok) * p.ldc;
+      uint8_t* srow = p.c_mx + (out_row0 + tok) * (p.N / 32);
+#pragma unroll
+      for (int j = 0; j < TN; j += 2) {
+        const int col0 = t.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32;
+        if (col0 >= p.N) continue;  // N % 32 == 0: a block is all in or all out
+        float h[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[4 * q + e] = silu_fast(scaled(i, j, q, e)) * scaled(i, j + 1, q, e);
+            amax = fmaxf(amax, fabsf(h[4 * q + e]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const uint32_t sc = mxfp8_scale_code(amax);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(uint32_t*)(crow + col0 + 8 * q + 4 * hi) =
+              mxfp8_pack4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], sc);
+        if (hi == 0) srow[col0 / 32] = (uint8_t)sc;
+      }
     } else if constexpr (EPI == EPI_BF16) {
       uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
 #pragma unroll
@@ -419,18 +471,19 @@ template <class SH, int EPI, bool GATHER, int GN, int WQ>
 __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   using GE = Geo<SH, WQ>;
   constexpr int BM = SH::BM, BN = SH::BN, WN = SH::WN, S = SH::S, SB = SH::SB, L = GE::L;
-  constexpr int TM = SH::TM, TN = SH::TN, KK = SH::KK, RPL = SH::RPL;
+  constexpr int TM = SH::TM, TN = SH::TN, KK = GE::KSUB, RPL = SH::RPL;
+  constexpr int A_STAGE = GE::A_STAGE, A_SC_LOADS = GE::A_SC_LOADS;
   constexpr int B_ROWB = GE::B_ROWB, B_RPL = GE::B_RPL, B_LOADS = GE::B_LOADS, B_CH = GE::B_CH;
   constexpr int ROWB = SH::ROWB, CH = SH::CH;
   constexpr int SC_LOADS = GE::SC_LOADS, B_STAGE = GE::B_STAGE;
   constexpr int SC_OFF = SH::BN * GE::B_ROWB;  // scale tile in a weight stage
-  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs W1 and W3 blocks");
+  static_assert(!is_swiglu(EPI) || TN % 2 == 0, "SwiGLU pairs W1 and W3 blocks");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wid / WN, wn = wid % WN;
   const int K = p.K, KT = K / SH::BK;
-  const int NT = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  const int NT = is_swiglu(EPI) ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int total_base =
       p.tile_start ? ld_uniform(p.tile_start, p.G) : (p.static_rows + BM - 1) / BM * NT;
   // split-K: ksplit consecutive copies of the tile list; copy ks reduces over its share of the
@@ -439,14 +492,17 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   const int nx = gridDim.x / 8, xcd = blockIdx.x % 8;
   const TailPlan plan = tail_plan(total_base * ks_n, xcd, nx, KT, p.tail_part && ks_n == 1);
   const int items = plan.pieces > 1 ? plan.full * nx + plan.tail * plan.pieces : plan.n;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * 2));
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a, (uint32_t)(p.a_rows * K * SH::AE));
+  // MXFP8 token rows: their E8M0 scales, row-major [a_rows, K / 32]
+  const __amdgpu_buffer_rsrc_t rAS = make_rsrc(GE::A8 ? (const void*)p.a_mx : p.a,
+                                               GE::A8 ? (uint32_t)(p.a_rows * (K / 32)) : 0u);
 
   const int l32 = lane & 31, hi = lane >> 5;
   const int sw = row_swizzle<CH>(l32), swb = row_swizzle<B_CH>(l32);
   const uint32_t a_frag = (uint32_t)((wm * SH::WTM + l32) * ROWB);
   const uint32_t b_frag = (uint32_t)((wn * SH::WTN + l32) * B_ROWB);
   char* const a_slots = smem;                      // S slots of A_BYTES
-  char* const b_slots = smem + S * SH::A_BYTES;    // SB slots of B_STAGE
+  char* const b_slots = smem + S * A_STAGE;        // SB slots of B_STAGE
 
   struct Tile {
     TileLoc loc;
@@ -478,6 +534,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   // per-lane source offsets of the current tile's loads (lane: row lane / 8, chunk lane % 8)
   uint32_t a_off[SH::A_LOADS], b_off[B_LOADS];
   uint32_t s_off[SC_LOADS > 0 ? SC_LOADS : 1];
+  uint32_t as_off[A_SC_LOADS > 0 ? A_SC_LOADS : 1];
   __amdgpu_buffer_rsrc_t rB, rB2, rS, rS2;
   int kt0 = 0, ktn = 0;
   auto setup = [&](const Tile& t) {
@@ -493,24 +550,24 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     const char* bbase =
         (const char*)(extra ? p.b_extra : p.b) + (extra ? 0 : (int64_t)wsel * gbytes);
     const char* b2base = bbase;
-    if (EPI == EPI_SWIGLU)
+    if (is_swiglu(EPI))
       b2base = (const char*)(extra ? p.b2_extra : p.b2) + (extra ? 0 : (int64_t)wsel * gbytes);
     const uint32_t b_bytes = (uint32_t)((int64_t)p.N * wrow);
     rB = make_rsrc(bbase, b_bytes);
     rB2 = make_rsrc(b2base, b_bytes);
-    if constexpr (WQ == kWMxfp4) {
+    if constexpr (GE::MX4) {
       // scales blocked by 32 rows: the dword of row r for 128-k step kt at
       // ((r / 32) * KT + kt) * 128 + (r % 32) * 4, so a block's 32 dwords are one line
       const int64_t sgroup = (int64_t)p.N * (K / 32);
       const uint8_t* sbase = extra ? p.b_mx_extra : p.b_mx + (int64_t)wsel * sgroup;
       const uint8_t* s2base = sbase;
-      if (EPI == EPI_SWIGLU) s2base = extra ? p.b2_mx_extra : p.b2_mx + (int64_t)wsel * sgroup;
+      if (is_swiglu(EPI)) s2base = extra ? p.b2_mx_extra : p.b2_mx + (int64_t)wsel * sgroup;
       rS = make_rsrc(sbase, (uint32_t)sgroup);
       rS2 = make_rsrc(s2base, (uint32_t)sgroup);
 #pragma unroll
       for (int i = 0; i < SC_LOADS; ++i) {
         const int n = (wid * SC_LOADS + i) * 32 + lane;  // lanes 32..63 load nothing
-        const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
+        const int src = is_swiglu(EPI) ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
         s_off[i] = lane < 32 && src < p.N ? (uint32_t)((src >> 5) * KT * 128 + (src & 31) * 4)
                                           : kOutOfRange;
       }
@@ -528,17 +585,28 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     for (int i = 0; i < SH::A_LOADS; ++i) {
       const int r = (wid * SH::A_LOADS + i) * RPL + lane / CH;
       const int c = (lane % CH) ^ row_swizzle<CH>(r);
-      a_off[i] = r < t.loc.rows_here ? (uint32_t)((int64_t)a_src[i] * K * 2) + c * 16 : kOutOfRange;
+      a_off[i] = r < t.loc.rows_here ? (uint32_t)((int64_t)a_src[i] * K * SH::AE) + c * 16 : kOutOfRange;
+    }
+    if constexpr (GE::A8) {
+      // the scale dword of tile row r for step kt sits at row * (K / 32) + kt * 4; lanes
+      // 32..63 and rows past the tile load nothing
+#pragma unroll
+      for (int i = 0; i < A_SC_LOADS; ++i) {
+        const int r = (wid * A_SC_LOADS + i) * 32 + l32;
+        const int prow = t.loc.row_base + t.loc.m0 + min(r, t.loc.rows_here - 1);
+        const int src = GATHER ? p.row_map[prow] : prow;
+        as_off[i] = lane < 32 && r < t.loc.rows_here ? (uint32_t)src * (uint32_t)(K / 32) : kOutOfRange;
+      }
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       // lane: weight row lane / (chunks per row), chunk lane % (chunks per row)
       const int n = (wid * B_LOADS + i) * B_RPL + lane / B_CH;
       const int c = (lane % B_CH) ^ row_swizzle<B_CH>(n);
-      const int src = EPI == EPI_SWIGLU ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
+      const int src = is_swiglu(EPI) ? t.loc.n_t * (BN / 2) + (n >> 6) * 32 + (n & 31) : t.loc.n_t * BN + n;
       // MXFP4 codes are blocked: row r's 64 bytes of 128-k step kt at ((r / 32) * KT + kt) * 2048
       // + (r % 32) * 64
-      const uint32_t row_at = WQ == kWMxfp4 ? (uint32_t)((src >> 5) * KT * 2048 + (src & 31) * 64)
+      const uint32_t row_at = GE::MX4 ? (uint32_t)((src >> 5) * KT * 2048 + (src & 31) * 64)
                                             : (uint32_t)(src * wrow);
       b_off[i] = src < p.N ? row_at + c * 16 : kOutOfRange;
     }
@@ -547,29 +615,37 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   // lk >= ktn loads nothing
   auto issue_a = [&](int lk, int slot) {
     const bool valid = lk < ktn;
-    char* sa = a_slots + slot * SH::A_BYTES;
+    char* sa = a_slots + slot * A_STAGE;
     const int kb = valid ? (kt0 + lk) * ROWB : 0;
 #pragma unroll
     for (int i = 0; i < SH::A_LOADS; ++i)
       load_lds16(rA, sa + (wid * SH::A_LOADS + i) * 1024, valid ? a_off[i] : kOutOfRange, kb);
+    if constexpr (GE::A8) {
+      // the stage's 4 scale bytes of each row (k-blocks (kt0 + lk) * 4 .. + 3)
+      const int kbs = valid ? (kt0 + lk) * 4 : 0;
+#pragma unroll
+      for (int i = 0; i < A_SC_LOADS; ++i)
+        load_lds4(rAS, sa + SH::A_BYTES + (wid * A_SC_LOADS + i) * 256,
+                  valid ? as_off[i] : kOutOfRange, kbs);
+    }
   };
   auto issue_b = [&](int lk, int bslot) {
     const bool valid = lk < ktn;
     char* sb = b_slots + bslot * B_STAGE;
-    const int kbw = valid ? (kt0 + lk) * (WQ == kWMxfp4 ? 32 * B_ROWB : B_ROWB) : 0;
+    const int kbw = valid ? (kt0 + lk) * (GE::MX4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int blk = wid * B_LOADS + i;
-      const bool second = EPI == EPI_SWIGLU && (((blk * B_RPL) >> 5) & 1);
+      const bool second = is_swiglu(EPI) && (((blk * B_RPL) >> 5) & 1);
       load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kbw);
     }
-    if constexpr (WQ == kWMxfp4) {
+    if constexpr (GE::MX4) {
       // the stage's 4 scale bytes of each row (k-blocks (kt0 + lk) * 4 .. + 3)
       const int kbs = valid ? (kt0 + lk) * 128 : 0;
 #pragma unroll
       for (int i = 0; i < SC_LOADS; ++i) {
         const int blk = wid * SC_LOADS + i;
-        const bool second = EPI == EPI_SWIGLU && (blk & 1);
+        const bool second = is_swiglu(EPI) && (blk & 1);
         load_lds4(second ? rS2 : rS, sb + SC_OFF + blk * 256, valid ? s_off[i] : kOutOfRange, kbs);
       }
     }
@@ -583,7 +659,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     for (int i = 0; i < B_LOADS; ++i) {
       if (i < i0 || i >= i1) continue;
       const int blk = wid * B_LOADS + i;
-      const bool second = EPI == EPI_SWIGLU && (((blk * B_RPL) >> 5) & 1);
+      const bool second = is_swiglu(EPI) && (((blk * B_RPL) >> 5) & 1);
       load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kbw);
     }
   };
@@ -609,34 +685,66 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 
   f32x16 acc[TM][TN];
   bf16x8 fa[2][TM], fb[2][TN];
+  // MXFP8 x MXFP4: 32 E4M3 codes per token lane, 32 E2M1 codes per weight lane, and the E8M0
+  // scale of the lane's k-block (lane half hi supplies block hi of the MFMA's 64 k)
+  i32x8 fa8[2][TM];
+  i32x4 fb4[2][TN];
+  int sca[2][TM], scb[2][TN];
   // NV: the wavefront's token blocks that hold rows of the tile (the others are skipped)
   auto read_frags = [&](auto nv, const char* sta, const char* st, int kk, int buf) {
     constexpr int NV = decltype(nv)::value;
-    const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
+    if constexpr (GE::A8) {
+      // sub-step kk covers k 64kk .. 64kk + 63 of the stage.  Token lane: k 64kk + 16hi .. + 15
+      // (chunk 4kk + hi of the 128-byte row) then k 64kk + 32 + 16hi .. + 15 (chunk 4kk + 2 +
+      // hi).  Weight lane: k 64kk + 32hi .. + 31 (chunk 2kk + hi of the 64-byte row).  Both take
+      // the scale of k-block 2kk + hi, byte 2kk + hi of the row's scale dword.
+      const int blk = 2 * kk + hi;
+      const uint32_t c0 = (uint32_t)(((4 * kk + hi) ^ sw) * 16);
+      const uint32_t c1 = (uint32_t)(((4 * kk + 2 + hi) ^ sw) * 16);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) fa[buf][i] = *(const bf16x8*)(sta + a_frag + coff + i * 32 * ROWB);
-    if constexpr (WQ == kWMxfp4) {
-      // a k-sub's 16 codes are half of chunk kk / 2 of the 64-byte row; the lane takes 8 of them
-      // (one dword) and the scale of their 32-block kk / 2
-      const uint32_t woff = (uint32_t)((((kk >> 1) ^ swb) * 16) + (kk & 1) * 8 + hi * 4);
+      for (int i = 0; i < NV; ++i) {
+        const char* ra = sta + a_frag + i * 32 * ROWB;
+        const i32x4 lo = *(const i32x4*)(ra + c0), up = *(const i32x4*)(ra + c1);
+        fa8[buf][i] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        const uint32_t s4 =
+            *(const uint32_t*)(sta + SH::A_BYTES + ((wm * SH::WTM) / 32 + i) * 256 + l32 * 4);
+        sca[buf][i] = (int)((s4 >> (8 * blk)) & 0xffu);
+      }
+      const uint32_t woff = (uint32_t)((blk ^ swb) * 16);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint32_t codes = *(const uint32_t*)(st + b_frag + woff + j * 32 * B_ROWB);
-        const uint32_t sc4 =
+        fb4[buf][j] = *(const i32x4*)(st + b_frag + woff + j * 32 * B_ROWB);
+        const uint32_t s4 =
             *(const uint32_t*)(st + SC_OFF + ((wn * SH::WTN) / 32 + j) * 256 + l32 * 4);
-        const float scale = __uint_as_float(((sc4 >> (8 * (kk >> 1))) & 0xffu) << 23);
-        fb[buf][j] = fp4x8_to_bf16(codes, scale);
+        scb[buf][j] = (int)((s4 >> (8 * blk)) & 0xffu);
       }
-    } else if constexpr (WQ == kWFp8) {
-      // a k-sub's 16 codes are chunk kk of the row; the lane takes half of it
-      const uint32_t woff = (uint32_t)(((kk ^ swb) * 16) + hi * 8);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[buf][j] = fp8x8_to_bf16(*(const uint2*)(st + b_frag + woff + j * 32 * B_ROWB));
     } else {
-      const uint32_t boff = (uint32_t)(((kk * 2 + hi) ^ swb) * 16);
+      const uint32_t coff = (uint32_t)(((kk * 2 + hi) ^ sw) * 16);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + boff + j * 32 * B_ROWB);
+      for (int i = 0; i < NV; ++i) fa[buf][i] = *(const bf16x8*)(sta + a_frag + coff + i * 32 * ROWB);
+      if constexpr (GE::MX4) {
+        // a k-sub's 16 codes are half of chunk kk / 2 of the 64-byte row; the lane takes 8 of them
+        // (one dword) and the scale of their 32-block kk / 2
+        const uint32_t woff = (uint32_t)((((kk >> 1) ^ swb) * 16) + (kk & 1) * 8 + hi * 4);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const uint32_t codes = *(const uint32_t*)(st + b_frag + woff + j * 32 * B_ROWB);
+          const uint32_t sc4 =
+              *(const uint32_t*)(st + SC_OFF + ((wn * SH::WTN) / 32 + j) * 256 + l32 * 4);
+          const float scale = __uint_as_float(((sc4 >> (8 * (kk >> 1))) & 0xffu) << 23);
+          fb[buf][j] = fp4x8_to_bf16(codes, scale);
+        }
+      } else if constexpr (WQ == kWFp8) {
+        // a k-sub's 16 codes are chunk kk of the row; the lane takes half of it
+        const uint32_t woff = (uint32_t)(((kk ^ swb) * 16) + hi * 8);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb[buf][j] = fp8x8_to_bf16(*(const uint2*)(st + b_frag + woff + j * 32 * B_ROWB));
+      } else {
+        const uint32_t boff = (uint32_t)(((kk * 2 + hi) ^ swb) * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8*)(st + b_frag + boff + j * 32 * B_ROWB);
+      }
     }
   };
   // weights as the first operand: D[column][token]
@@ -645,8 +753,18 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (GE::A8) {
+          // v_mfma_scale_f32_32x32x64_f8f6f4: first operand E2M1 (format 4, registers 0-3),
+          // second E4M3 (format 0), each with its lane's E8M0 scale
+          const i32x4 w = fb4[buf][j];
+          const i32x8 wa = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wa, fa8[buf][i], acc[i][j], 4, 0, 0, scb[buf][j], 0, sca[buf][i]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+        }
+      }
   };
   // Every step issues L loads per wavefront (stage lk + S, masked past the end), so when step
   // lk waits for stage lk + 1 exactly S - 2 stages were issued after it.
@@ -655,9 +773,9 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     read_frags(nv, a_slots, b_slots, 0, 0);
     issue_both(S - 1, S - 1, SB - 1, SB - 1);
     for (int lk = 0; lk < ktn; ++lk) {
-      const char* cura = a_slots + (lk % S) * SH::A_BYTES;
+      const char* cura = a_slots + (lk % S) * A_STAGE;
       const char* curb = b_slots + (lk % SB) * B_STAGE;
-      const char* nxta = a_slots + ((lk + 1) % S) * SH::A_BYTES;
+      const char* nxta = a_slots + ((lk + 1) % S) * A_STAGE;
       const char* nxtb = b_slots + ((lk + 1) % SB) * B_STAGE;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -682,6 +800,19 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
             issue_b_part(lk - 1 + SB, (lk - 1) % SB, kk * BPER, (kk + 1) * BPER);
         }
         mfmas(nv, kk & 1);
+        if constexpr (GE::A8) {
+          // few, long MFMAs per sub-step: the next sub-step's reads (3 per token block, 2 per
+          // weight block) and, in the last, the stage's L loads, spread evenly over them
+          constexpr int NM = NV * TN > 0 ? NV * TN : 1;
+          constexpr int RD = (3 * NV + 2 * TN + NM - 1) / NM, LD = (L + NM - 1) / NM;
+#pragma unroll
+          for (int m = 0; m < NV * TN; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+            if (kk == KK - 1) __builtin_amdgcn_sched_group_barrier(0x020, LD, 0);
+          }
+          continue;
+        }
         // interleave: one MFMA, then one LDS read and one global load
 #pragma unroll
         for (int m = 0; m < NV * TN; ++m) {
@@ -817,7 +948,7 @@ static hipError_t run(const GroupedGemm& p, int max_tiles, int num_cus, hipStrea
   // workgroups per CU: as many as the LDS holds, at most 8 wavefronts per CU (12 for the MXFP4
   // tiles, whose wavefronts need few enough registers for three per SIMD)
   int per_cu = (160 * 1024) / LDS;
-  const int by_waves = (WQ == kWMxfp4 ? 12 : 8) / SH::WAVES;
+  const int by_waves = (Geo<SH, WQ>::MX4 ? 12 : 8) / SH::WAVES;
   if (per_cu > by_waves) per_cu = by_waves;
   if (per_cu < 1) per_cu = 1;
   int grid = num_cus * per_cu;
@@ -866,6 +997,7 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   int bm, nt;
   gemm_bf16_tiling(kind, avg_rows_per_group, p.N, &bm, &nt);
   if (p.ksplit > 1 && kind != GEMM_GATE) return hipErrorInvalidValue;  // fp32 output only
+  if (p.a_mx && kind == GEMM_GATE) return hipErrorInvalidValue;
   if (kind == GEMM_GATE) bm = gemm_gate_bm(p.static_rows, p.N, p.ksplit > 1);
   // upper bound of the tile count (the exact count is on the device)
   int64_t max_tiles;
@@ -889,6 +1021,18 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GroupedGemm& p, int avg_rows_pe
   }
   const bool big = bm == PrefillShape::BM;
   const bool gather = p.row_map != nullptr;
+  if (p.a_mx) {  // MXFP8 token rows: MXFP4 weights only, the 32-row shape
+    if (!p.b_mx || p.K % 128 || (kind == GEMM_GATE_UP && (!p.b2_mx || !p.c_mx || p.N % 32)))
+      return hipErrorInvalidValue;
+    if (p.G > p.G_routed && (!p.b_mx_extra || (kind == GEMM_GATE_UP && !p.b2_mx_extra)))
+      return hipErrorInvalidValue;
+    if (bm != ShapeMx4A8::BM) return hipErrorInvalidValue;
+    if (kind == GEMM_GATE_UP)
+      return gather ? run<ShapeMx4A8, EPI_SWIGLU_MX8, true, 1, kWMx4A8>(p, mt, num_cus, s)
+                    : run<ShapeMx4A8, EPI_SWIGLU_MX8, false, 1, kWMx4A8>(p, mt, num_cus, s);
+    if (gather) return hipErrorInvalidValue;
+    return run<ShapeMx4A8, EPI_BF16, false, 1, kWMx4A8>(p, mt, num_cus, s);
+  }
   if (p.b_mx) {  // MXFP4 weights: the 32-row shape for every group size, K % 128 == 0
     if (p.K % 128 || (kind == GEMM_GATE_UP && !p.b2_mx)) return hipErrorInvalidValue;
     if (p.G > p.G_routed && (!p.b_mx_extra || (kind == GEMM_GATE_UP && !p.b2_mx_extra)))

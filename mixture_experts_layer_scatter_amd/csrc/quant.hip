@@ -164,6 +164,67 @@ hipError_t launch_quantize_mxfp4(const void* w, int bf16, int64_t rows, int K, u
   return hipGetLastError();
 }
 
+// MXFP8 activations: one thread per block of 32 consecutive elements of a row; the codes stay
+// row-major (32 bytes per block, two 16-byte stores) and so do the scales (one byte per block).
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const void* __restrict__ x,
+                                                             int64_t blocks,
+                                                             uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ scales) {
+  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < blocks;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    float v[32];
+    if constexpr (BF16) {
+      const uint4* src = (const uint4*)((const uint16_t*)x + b * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = src[i];
+        const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = __uint_as_float(h[j] << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float(h[j] & 0xffff0000u);
+        }
+      }
+    } else {
+      const float4* src = (const float4*)((const float*)x + b * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 f = src[i];
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t code = mxfp8_scale_code(amax);
+    uint32_t w[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      w[d] = amax > 0.f ? mxfp8_pack4(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3], code) : 0u;
+    uint4* dst = (uint4*)(q + b * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[b] = (uint8_t)code;
+  }
+}
+
+hipError_t launch_quantize_mxfp8(const void* x, int bf16, int64_t rows, int K, uint8_t* q,
+                                 uint8_t* scales, hipStream_t s) {
+  const int64_t blocks = rows * (K / 32);
+  if (blocks <= 0) return hipSuccess;
+  const int64_t g = (blocks + 255) / 256;
+  const int grid = g < 65536 ? (int)g : 65536;
+  if (bf16)
+    quantize_mxfp8_kernel<true><<<grid, 256, 0, s>>>(x, blocks, q, scales);
+  else
+    quantize_mxfp8_kernel<false><<<grid, 256, 0, s>>>(x, blocks, q, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uint8_t* q,
                                float* scales, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

@@ -80,9 +80,10 @@ def check_routing_changes(w, r, g_ids, g_logits):
     return changed
 
 
-def check_against_oracle(w, g, weights, shared, tag=""):
+def check_against_oracle(w, g, weights, shared, tag="", ffn=None):
     """Steps 1-5 above for the GPU run g of workload w; weights / shared: the expert weights
-    the layer computes with, as the oracle sees them."""
+    the layer computes with, as the oracle sees them; ffn: the oracle's expert FFN (the plain
+    one unless given)."""
     x = moe_synth.x(w)
     log("  oracle routing (gate on every token)")
     r = routing(w, x)
@@ -118,7 +119,7 @@ def check_against_oracle(w, g, weights, shared, tag=""):
     route = dict(ids=rg["ids"], pos=rg["pos"], w=r["w"].copy())
     route["w"][changed] = rg["w"][changed]
     log(f"  oracle FFN on {w.T} tokens")
-    ref = layer_tokens(w, x, route, np.arange(w.T), weights, shared)
+    ref = layer_tokens(w, x, route, np.arange(w.T), weights, shared, ffn=ffn)
     err = rel_l2(g["y"], ref)
     rec = dict(T=w.T, changed=len(changed), near_ties=near,
                min_margin=float(r["margin"].min()) if w.T else float("inf"),

@@ -97,12 +97,15 @@ def _experts_ahead(weights: Weights, experts, window: int = 16):
             yield e, f.result()
 
 
-def layer_tokens(w: moe_synth.Workload, x, route, tokens, weights: Weights, shared=None):
+def layer_tokens(w: moe_synth.Workload, x, route, tokens, weights: Weights, shared=None,
+                 ffn=None):
     """float64 outputs y[tokens] of the layer, given a full routing (ids, w, pos).
 
     Runs each needed expert only on the selected tokens' kept slots and sums in
-    slot order (oracle.combine); the always-on expert is added when present.
+    slot order (oracle.combine); the always-on expert is added when present.  ffn: the
+    oracle's expert FFN to apply (oracle.expert_ffn unless given).
     """
+    ffn = oracle.expert_ffn if ffn is None else ffn
     tokens = np.asarray(tokens, np.int64)
     n, k, H = len(tokens), w.k, w.H
     pos = route["pos"][tokens]
@@ -118,11 +121,11 @@ def layer_tokens(w: moe_synth.Workload, x, route, tokens, weights: Weights, shar
     for e, (w1, w3, w2) in _experts_ahead(weights, sorted(need)):
         lst = need[e]
         rows = x[tokens[[i for (i, j) in lst]]]
-        out = oracle.expert_ffn(rows, w1, w3, w2)
+        out = ffn(rows, w1, w3, w2)
         for r, (i, j) in enumerate(lst):
             yp[i * k + j] = out[r]
             sub_pos[i, j] = i * k + j
     ys = None
     if shared is not None:
-        ys = oracle.expert_ffn(x[tokens], *shared)
+        ys = ffn(x[tokens], *shared)
     return oracle.combine(yp, sub_pos, wts, ys)

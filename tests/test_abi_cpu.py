@@ -232,6 +232,40 @@ def test_mxfp4_entry_point_checks():
                                        1 << 40, None) == L.MOE_ERR_UNSUPPORTED
 
 
+def test_w4a8_entry_point_checks():
+    """MXFP8 activations: the quantiser takes rows of K % 32 == 0; the FFN and the layer need
+    the MXFP4 scales, bf16 layers and H, I multiples of 128, all checked before any launch."""
+    L = _lib()
+    lib = L.lib()
+    p = C.c_void_p(16)  # never dereferenced
+    assert lib.moe_quantize_mxfp8(4, 48, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_mxfp8(4, 0, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8(-1, 32, L.MOE_BF16, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8(4, 32, 5, p, p, p, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8(4, 32, L.MOE_F32, p, p, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8(0, 32, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    d = _dims()  # H = I = 128
+    assert lib.moe_expert_ffn_w4a8(C.byref(d), p, p, p, None, p, p, p, p, p, p, 1 << 40,
+                                   None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_w4a8(C.byref(_dims(I=192)), p, p, p, p, p, p, p, p, p, p, 1 << 40,
+                                   None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_w4a8(C.byref(d), p, p, p, p, p, p, p, p, p, p, 16,
+                                   None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_forward_w4a8(C.byref(_dims(H=192)), *([p] * 16), None, p, 1 << 40,
+                                      None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_forward_w4a8(C.byref(_dims(dtype=L.MOE_F32)), *([p] * 16), None, p,
+                                      1 << 40, None) == L.MOE_ERR_UNSUPPORTED
+    args = [p] * 16
+    args[4] = None  # w1s
+    assert lib.moe_layer_forward_w4a8(C.byref(d), *args, None, p, 1 << 40,
+                                      None) == L.MOE_ERR_INVALID_ARG
+    # a shared expert needs its scales too
+    args = [p] * 16
+    args[10] = None  # ws1s
+    assert lib.moe_layer_forward_w4a8(C.byref(_dims(I_shared=128)), *args, None, p, 1 << 40,
+                                      None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_static_scratch_entry_point_checks():
     """moe_layer_forward_static (no workspace argument): the size of its library-owned scratch,
     dims rejected with the same codes as moe_layer_forward, and dims whose workspace exceeds
