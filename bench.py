@@ -21,6 +21,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the block-scaled fp8 x fp4 product runs at it)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 METRIC = "MoE-layer tokens/s on 1 GPU; MFMA % peak (prefill), HBM GB/s % peak (decode)"
 
@@ -37,9 +38,10 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="one workload to time (default: mixtral_prefill, followed by the "
                          "--sub-workloads as sub-results)")
-    ap.add_argument("--weights", choices=("same", "fp8", "mxfp4"), default="same",
+    ap.add_argument("--weights", choices=("same", "fp8", "mxfp4", "w4a8"), default="same",
                     help="expert weights in the layer's storage type, FP8 E4M3 with per-row "
-                         "scales, or MXFP4 (quantised once before timing; bf16 layers)")
+                         "scales, MXFP4, or MXFP4 on MXFP8 activations (weights quantised once "
+                         "before timing; bf16 layers)")
     ap.add_argument("--cache-slots", type=int, default=0,
                     help="also measure the layer with its routed experts in an HBM expert cache "
                          "of this many slots, filled from pinned host memory (cold and warm)")
@@ -142,7 +144,8 @@ def measure(w, args, steps, warmup, cache_slots=0):
     sh = stream.cuda_stream
 
     fp8 = args.weights == "fp8"
-    mx = args.weights == "mxfp4"
+    a8 = args.weights == "w4a8"        # MXFP4 weights on MXFP8 activations
+    mx = args.weights == "mxfp4" or a8
     lowbit = fp8 or mx
     quant_err = None
     if lowbit:
@@ -160,11 +163,13 @@ def measure(w, args, steps, warmup, cache_slots=0):
             t[k] = None
         t["shared"] = None
         torch.cuda.empty_cache()
-        log("expert weights quantised to " + ("MXFP4" if mx else "FP8 E4M3 (per-row scales)"))
+        log("expert weights quantised to " + ("MXFP4" if mx else "FP8 E4M3 (per-row scales)")
+            + (", activations MXFP8" if a8 else ""))
 
     def step(debug=None):
         if lowbit:
-            fwd = moe.layer_forward_mxfp4 if mx else moe.layer_forward_fp8
+            fwd = (moe.layer_forward_w4a8 if a8 else moe.layer_forward_mxfp4 if mx
+                   else moe.layer_forward_fp8)
             fwd(d, t["x"], t["wg"], t["bias"], q["w1"], q["w3"], q["w2"], q_sh, y=y, ws=ws,
                 debug=debug)
         else:
@@ -261,24 +266,31 @@ def measure(w, args, steps, warmup, cache_slots=0):
          + 3.0 * w.H * Is * wes + sc(2 * Is + w.H if Is else 0) + w.E * w.H * es
          + 2.0 * w.T * w.H * es)
     gu_avg = float(np.mean(gu_ms))
+    # MFMA peak of the expert GEMMs: bf16, or fp8 for the MXFP8 x MXFP4 product
+    peak_x = PEAK_FP8_TFLOPS if a8 else PEAK_BF16_TFLOPS
+    # bytes of a token-row element the expert GEMMs read (MXFP8: code and 1/32 of a scale)
+    xes = 1.0 + 1.0 / 32 if a8 else es
     # the gate-up kernel's bound: whichever of its algorithmic flops at the MFMA peak and its
     # algorithmic bytes (W1 and W3 of every touched expert and the shared expert, read once, and
-    # x) at the HBM peak takes longer
+    # the token rows) at the HBM peak takes longer
     gu_bytes = (2.0 * w.H * w.I * wes * touched + sc(2 * w.I * touched) + 2.0 * w.H * Is * wes
-                + sc(2 * Is) + w.T * w.H * es)
+                + sc(2 * Is) + w.T * w.H * xes)
     gu_flops = 4.0 * R * w.H * w.I + 4.0 * w.T * w.H * Is
-    if gu_bytes / (PEAK_HBM_GBS * 1e9) > gu_flops / (PEAK_BF16_TFLOPS * 1e12):
+    if gu_bytes / (PEAK_HBM_GBS * 1e9) > gu_flops / (peak_x * 1e12):
         achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
         achieved = gu_flops / (gu_avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["traffic"] = profiled_traffic(w.name + ("_fp8" if fp8 else "_mxfp4" if mx else ""))
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_x,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_x, 4), "traffic": None}
+    roof["traffic"] = profiled_traffic(
+        w.name + ("_fp8" if fp8 else "_w4a8" if a8 else "_mxfp4" if mx else ""))
     # the library takes 256-row tiles when a group holds >= 128 rows on average
     # (the timed span is the grouped GEMM plus the reduction of its split last round of tiles)
-    if mx:
+    if a8:
+        shape, rows = "TileShape<32,256,1,4,2,128,2,1>", "32-row tiles"
+    elif mx:
         shape, rows = "TileShape<32,256,1,4,2,128>", "32-row tiles"
     else:
         big = ("TileShape<256,256,2,4,2>" if fp8
@@ -289,22 +301,27 @@ def measure(w, args, steps, warmup, cache_slots=0):
             shape, rows = small, "32-row tiles"
         else:
             shape, rows = big, "256x256 tiles"
-    tag = ", FP8 weights" if fp8 else ", MXFP4 weights" if mx else ""
+    tag = (", FP8 weights" if fp8 else ", MXFP4 weights x MXFP8 activations" if a8
+           else ", MXFP4 weights" if mx else "")
     roof["kernel"] = (f"gemm_kernel<{shape}, SwiGLU{tag}> + gemm_tail_kernel "
                       f"(grouped gate-up, {rows})")
     roof["avg_launch_ms"] = round(gu_avg, 4)
     layer_s = ms_per_step * 1e-3
-    layer_frac = max(F / (PEAK_BF16_TFLOPS * 1e12), B / (PEAK_HBM_GBS * 1e9)) / layer_s
+    # the gate's flops at the bf16 peak, the experts' at theirs
+    F_gate = 2.0 * w.T * w.H * w.E
+    t_mfma = F_gate / (PEAK_BF16_TFLOPS * 1e12) + (F - F_gate) / (peak_x * 1e12)
+    layer_frac = max(t_mfma, B / (PEAK_HBM_GBS * 1e9)) / layer_s
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
               "compute_units": props.multi_processor_count, "hip": torch.version.hip}
 
-    layer_bound = ("mfma" if F / (PEAK_BF16_TFLOPS * 1e12) >= B / (PEAK_HBM_GBS * 1e9) else "hbm")
+    layer_bound = "mfma" if t_mfma >= B / (PEAK_HBM_GBS * 1e9) else "hbm"
     config = {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
               "I_shared": Is, "capacity": cap, "accumulate": "fp32",
               **({"bias_mode": args.bias_mode} if w.zipf_s is not None else {}),
               **({"expert_weights": "fp8_e4m3_per_row_scale"} if fp8 else {}),
-              **({"expert_weights": "mxfp4_e2m1_e8m0_per_32"} if mx else {})}
+              **({"expert_weights": "mxfp4_e2m1_e8m0_per_32"} if mx else {}),
+              **({"expert_activations": "mxfp8_e4m3_e8m0_per_32"} if a8 else {})}
     layer = {"flops": F, "bytes": B, "tflops": round(F / layer_s / 1e12, 1),
              "ms_median": round(float(np.median(layer_ms)), 4),
              "ms_min": round(float(np.min(layer_ms)), 4),

@@ -255,7 +255,9 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const uint8_t* a_m
   // groups past G_routed take the extra weights; there must be some for them, stored like W's
   if (G_routed < 0 || G_routed > G || !W.complete() || (W.fmt() && !bf16)) return hipErrorInvalidValue;
   if (G > G_routed && (!X || !X->complete() || X->fmt() != W.fmt())) return hipErrorInvalidValue;
-  if (W.mx()) avg_rows = 0;  // MXFP4 runs on the 32-row tiles for every group size
+  // MXFP4 weights on bf16 rows run on the 32-row tiles for every group size; on MXFP8 rows the
+  // tiles follow the group size as for bf16
+  if (W.mx() && !W.a8) avg_rows = 0;
   if (W.a8 != (a_mx != nullptr)) return hipErrorInvalidValue;
   uint8_t* act_mx = W.a8 ? (uint8_t*)act + align_up((size_t)max_rows * I) : nullptr;
   if (group_slot && !bf16) return hipErrorInvalidValue;  // slot indirection: MFMA path only

@@ -20,7 +20,7 @@ import torch
 import moe_synth
 import oracle
 from layer_check import check_against_oracle, run_layer
-from gpu_util import bf16_normal, dev, f64, log, need_gpu, rel_l2
+from gpu_util import bf16_normal, dev, f64, log, need_gpu, rel_l2, split_tail_pieces
 from oracle_steps import Mxfp4Weights, mxfp4_dequantised
 from moe_synth.device import workload_tensors
 
@@ -105,14 +105,31 @@ def _ffn_case(counts, H, I, seed=0):
     ([5], 128, 128),
     ([0, 1, 31, 33, 7, 0, 64, 2], 128, 384),           # ragged 32-row tiles, a column tail
     ([8] * 64, 1024, 512),                              # decode-like: many small groups
-    ([300, 0, 513, 7, 256], 256, 384),                  # large groups on 32-row tiles
+    ([300, 0, 513, 7, 256], 256, 384),                  # 256 x 256 tiles, ragged groups
     ([300, 280, 270, 310], 2048, 1024),
-    ([520] * 6, 4096, 2048),                            # a split last round of tiles
+    ([40, 90, 100], 2048, 1024),                        # 32-row tiles, 2 and 3 row blocks
 ])
 def test_expert_ffn_w4a8(counts, H, I):
     need_gpu()
     log(f"expert_ffn w4a8 counts={counts[:8]} H={H} I={I}")
     got, ref = _ffn_case(counts, H, I, seed=len(counts) + I)
+    err = rel_l2(got, ref)
+    row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    log(f"  rel-L2 {err:.3g}, worst row {row_err.max():.3g}")
+    assert err <= 2e-2
+    assert (row_err <= 2e-2).all()
+
+
+def test_expert_ffn_w4a8_split_tail():
+    """256 x 256 MXFP8 tiles whose last, partly filled round of tiles is cut into k-ranges in
+    both GEMMs (the schedule mirrored in split_tail_pieces, with 128-k steps)."""
+    need_gpu()
+    counts, H, I = [520] * 6, 4096, 2048
+    gu = split_tail_pieces(counts, H, (I + 127) // 128, bk=128)
+    dn = split_tail_pieces(counts, I, (H + 255) // 256, bk=128)
+    log(f"expert_ffn w4a8 (split tail round): pieces per XCD gate-up {gu}, down {dn}")
+    assert max(gu) > 1 and max(dn) > 1
+    got, ref = _ffn_case(counts, H, I, seed=13)
     err = rel_l2(got, ref)
     row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
     log(f"  rel-L2 {err:.3g}, worst row {row_err.max():.3g}")
@@ -146,6 +163,13 @@ def check_layer_w4a8(w):
 def test_layer_w4a8_reduced_tokens_every_token(name, T):
     need_gpu()
     check_layer_w4a8(moe_synth.get(name).scaled(T))
+
+
+def test_layer_w4a8_prefill_tiles_every_token():
+    """The Mixtral-shaped layer at 1024 tokens: 256 rows per expert on average, so the expert
+    GEMMs take the 256 x 256 MXFP8 tiles."""
+    need_gpu()
+    check_layer_w4a8(moe_synth.get("mixtral_prefill").scaled(1024))
 
 
 def test_layer_w4a8_full_size_decode_every_token():
