@@ -48,9 +48,12 @@ def main():
     ap.add_argument("--bias-mode", choices=("softmax", "select"), default="softmax",
                     help="how a workload's routing bias enters: inside the softmax, or ranking only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sub-workloads", default="qwen3_prefill,dsv3_decode,skewed_capacity",
+    ap.add_argument("--sub-workloads",
+                    default="qwen3_prefill,dsv3_decode,skewed_capacity,dsv3_decode:w4a8,"
+                            "mixtral_prefill:w4a8",
                     help="other workloads timed after the default one (no --workload given) and "
-                         "reported under sub_results (empty: none)")
+                         "reported under sub_results; name:weights selects the expert weight "
+                         "format (as --weights; default same) (empty: none)")
     ap.add_argument("--sub-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -101,11 +104,12 @@ def main():
     # capacity drops; each with its own dominant-kernel roofline and layer fraction
     if args.sub_workloads and default_run and args.weights == "same":
         subs = {}
-        for name in [n for n in args.sub_workloads.split(",") if n]:
+        for spec in [n for n in args.sub_workloads.split(",") if n]:
             torch.cuda.empty_cache()
+            name, _, wt = spec.partition(":")
             sw = moe_synth.get(name)
-            sr = measure(sw, args, args.sub_steps, args.warmup)
-            subs[name] = {"config": sr["config"], "ms_per_step": sr["ms_per_step"],
+            sr = measure(sw, args, args.sub_steps, args.warmup, weights=wt or "same")
+            subs[spec] = {"config": sr["config"], "ms_per_step": sr["ms_per_step"],
                           "tokens_per_s": sr["tokens_per_s"], "roofline": sr["roofline"],
                           "layer_roofline_frac": sr["layer"]["roofline_frac"],
                           "layer_bound": sr["layer"]["bound"],
@@ -113,7 +117,9 @@ def main():
                           "stage_ms": sr["layer"]["stage_ms"],
                           "kept_rows": sr["layer"]["kept_rows"],
                           "experts_touched": sr["layer"]["experts_touched"],
-                          "near_tie_tokens": sr["layer"]["near_tie_tokens"]}
+                          "near_tie_tokens": sr["layer"]["near_tie_tokens"],
+                          **({k: sr["layer"][k] for k in ("lowbit_vs_bf16_weights_rel_l2",)
+                              if k in sr["layer"]})}
         out["sub_results"] = subs
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
@@ -121,9 +127,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure(w, args, steps, warmup, cache_slots=0):
+def measure(w, args, steps, warmup, cache_slots=0, weights=None):
     """Time `steps` fused layer forwards of workload w (after `warmup` untimed ones) with the
-    inputs resident in HBM; returns the numbers of one JSON record."""
+    inputs resident in HBM and the expert weights in format `weights` (args.weights unless
+    given); returns the numbers of one JSON record."""
+    weights = args.weights if weights is None else weights
     import numpy as np
     import torch
 
@@ -143,14 +151,14 @@ def measure(w, args, steps, warmup, cache_slots=0):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    fp8 = args.weights == "fp8"
-    a8 = args.weights == "w4a8"        # MXFP4 weights on MXFP8 activations
-    mx = args.weights == "mxfp4" or a8
+    fp8 = weights == "fp8"
+    a8 = weights == "w4a8"        # MXFP4 weights on MXFP8 activations
+    mx = weights == "mxfp4" or a8
     lowbit = fp8 or mx
     quant_err = None
     if lowbit:
         if w.dtype != "bf16":
-            sys.exit(f"--weights {args.weights} needs a bf16 workload")
+            sys.exit(f"--weights {weights} needs a bf16 workload")
         # reference output with the bf16 weights, then quantise and drop them
         moe.layer_forward(d, t["x"], t["wg"], t["bias"], t["w1"], t["w3"], t["w2"], t["shared"],
                           y=y, ws=ws)
