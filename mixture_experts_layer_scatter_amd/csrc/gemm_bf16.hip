@@ -58,6 +58,10 @@
 //    lines); the code and scale tiles travel into LDS, and
 //    a fragment read widens 8 codes with the hardware's scaled conversion (the
 //    products are exact in bf16), so the scales never reach the epilogue.
+//  * MXFP4 weights on MXFP8 token rows (WQ = 3, "MoE 推理架构深度实战" §5.2's 4-bit weights
+//    with FP8 activations): both operands stay in their codes and the block-scaled MFMA
+//    (v_mfma_scale_f32_32x32x64_f8f6f4) applies each lane's E8M0 scales; the gate-up epilogue
+//    quantises silu(a) * g to MXFP8 for the down GEMM (EPI_SWIGLU_MX8).
 //  * FP8 weights (WQ = 1): the weight tile travels HBM -> LDS as E4M3 bytes (half
 //    the bytes of bf16, the point for the weight-streaming decode shape); a
 //    fragment read takes 8 codes and widens them to bf16 in registers (every
