@@ -271,7 +271,7 @@ using ShapeMx4A8 = TileShape<32, 256, 1, 4, 2, 128, 2, 1>;
 // operands (52 KB each).  Wavefront tiles of 64 token rows x 128 columns: per 64-k MFMA step a
 // token block takes two 16-byte LDS reads per lane and a weight block one, so four weight blocks
 // and two token blocks (10 reads for 8 MFMAs) beat the 128 x 64 split of the bf16 shape
-using PrefillShapeMx4A8 = TileShape<256, 256, 4, 2, 2, 128, 2, 1>;
+using PrefillShapeMx4A8 = TileShape<256, 256, 4, 2, 2, 128, 3, 1>;
 
 // ---- tile bookkeeping shared by the GEMM and its tail reduction ---------------------------------
 
@@ -659,17 +659,28 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       }
     }
   };
-  // weight loads [i0, i1) of step lk into slot bslot (bf16 or FP8 weights, no scale tiles)
+  // weight-side loads [i0, i1) of step lk into slot bslot: the weight tile's B_LOADS, then (E2M1
+  // weights) its SC_LOADS scale loads
   auto issue_b_part = [&](int lk, int bslot, int i0, int i1) {
     const bool valid = lk < ktn;
     char* sb = b_slots + bslot * B_STAGE;
-    const int kbw = valid ? (kt0 + lk) * B_ROWB : 0;
+    const int kbw = valid ? (kt0 + lk) * (GE::MX4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       if (i < i0 || i >= i1) continue;
       const int blk = wid * B_LOADS + i;
       const bool second = is_swiglu(EPI) && (((blk * B_RPL) >> 5) & 1);
       load_lds16(second ? rB2 : rB, sb + blk * 1024, valid ? b_off[i] : kOutOfRange, kbw);
+    }
+    if constexpr (GE::MX4) {
+      const int kbs = valid ? (kt0 + lk) * 128 : 0;
+#pragma unroll
+      for (int i = 0; i < SC_LOADS; ++i) {
+        if (B_LOADS + i < i0 || B_LOADS + i >= i1) continue;
+        const int blk = wid * SC_LOADS + i;
+        const bool second = is_swiglu(EPI) && (blk & 1);
+        load_lds4(second ? rS2 : rS, sb + SC_OFF + blk * 256, valid ? s_off[i] : kOutOfRange, kbs);
+      }
     }
   };
   // The step-lk barrier sends out the token rows of step lk + S and (with S == SB) the weights of
@@ -812,7 +823,9 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
         // reach the L1 in a steadier stream (3 % faster on both prefill workloads than all of a
         // stage's loads issued in one sub-step; one load per two MFMAs was slower).  Step
         // lk + 1's barrier still waits for all but these (WAIT = LB).
-        constexpr int BSPAN = 2, BPER = (GE::LB + BSPAN - 1) / BSPAN;
+        // (MXFP8 stages have two sub-steps, the second holding the barrier: all of the weight
+        // stage goes out in the first, so that the barrier's wait count stays LB)
+        constexpr int BSPAN = GE::A8 ? 1 : 2, BPER = (GE::LB + BSPAN - 1) / BSPAN;
         if constexpr (S < SB) {
           if (kk < BSPAN && lk > 0)
             issue_b_part(lk - 1 + SB, (lk - 1) % SB, kk * BPER, (kk + 1) * BPER);
@@ -824,14 +837,16 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
         }
         if constexpr (GE::A8) {
           // few, long MFMAs per sub-step: the next sub-step's reads (3 per token block, 2 per
-          // weight block) and, in the last, the stage's L loads, spread evenly over them
+          // weight block) and the sub-step's global loads spread evenly over them
           constexpr int NM = NV * TN > 0 ? NV * TN : 1;
-          constexpr int RD = (3 * NV + 2 * TN + NM - 1) / NM, LD = (L + NM - 1) / NM;
+          constexpr int RD = (3 * NV + 2 * TN + NM - 1) / NM;
+          constexpr int LDL = (S < SB ? GE::LA : L), LDB = S < SB ? GE::LB : 0;
 #pragma unroll
           for (int m = 0; m < NV * TN; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-            if (kk == KK - 1) __builtin_amdgcn_sched_group_barrier(0x020, LD, 0);
+            if (kk == KK - 1) __builtin_amdgcn_sched_group_barrier(0x020, (LDL + NM - 1) / NM, 0);
+            if (kk == 0 && LDB > 0) __builtin_amdgcn_sched_group_barrier(0x020, (LDB + NM - 1) / NM, 0);
           }
           continue;
         }
