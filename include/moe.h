@@ -25,6 +25,8 @@
  *    read the per-expert row counts back (so it cannot be captured into a HIP
  *    graph).  The cache's bookkeeping calls (moe_cache_create, _destroy,
  *    _slots) are host-only.
+ *  - Device arrays start on 16-byte boundaries (hipMalloc and torch's
+ *    allocator give 256): the kernels move rows with 16-byte vector accesses.
  *  - Layouts are row-major and contiguous.  Weights use the [out, in] layout
  *    of a linear layer, so both GEMM operands are contiguous along the
  *    reduction dimension.
