@@ -127,6 +127,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// Two quads of bf16 outputs of a token row, as the MFMA leaves them: lane half hi holds
+// columns 4hi .. 4hi + 3 of quad a (dwords a0, a1) and of quad b, 8 columns further (b0, b1).
+// One v_permlane32_swap per dword pair trades lane half 0's quad b for half 1's quad a, so
+// lane half 0 ends with columns 0 .. 7 and half 1 with columns 8 .. 15: one 16-byte store per
+// lane at column 8hi, in place of two 8-byte stores.
+__device__ __forceinline__ uint4 swap_halves(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1) {
+  // lanes 0..31 keep a and take lanes 32..63's a; lanes 32..63 keep b and take lanes 0..31's b
+  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  return make_uint4(s0[0], s1[0], s0[1], s1[1]);
+}
+
 // Swizzle of the 16-byte chunks of an LDS row of CH chunks (chunk c of row r sits at c ^
 // swizzle(r)): the 8 (and the 16) consecutive rows that one fragment read serves per cycle fall
 // in distinct banks.  It depends on bits 0..4 of the row only, so the rows of a fragment's
@@ -394,7 +406,23 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
       uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
       // blocks j (W1) and j + 1 (W3) hold the same 32 columns
 #pragma unroll
-      for (int j = 0; j < TN; j += 2)
+      for (int j = 0; j < TN; j += 2) {
+        const int col0 = t.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32;
+        if (col0 + 32 <= p.N) {  // a whole block (the lane pair of the token row agrees)
+          uint32_t d[4][2];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = silu_fast(scaled(i, j, q, e)) * scaled(i, j + 1, q, e);
+            d[q][0] = pack_bf16x2(h[0], h[1]);
+            d[q][1] = pack_bf16x2(h[2], h[3]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q += 2)
+            *(uint4*)(crow + col0 + 8 * q + 8 * hi) = swap_halves(d[q][0], d[q][1], d[q + 1][0], d[q + 1][1]);
+          continue;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = t.n_t * (BN / 2) + wn * (SH::WTN / 2) + (j / 2) * 32 + 8 * q + 4 * hi;
@@ -408,6 +436,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
             *(uint2*)(crow + col) = v;
           }
         }
+      }
     } else if constexpr (EPI == EPI_SWIGLU_MX8) {
       // MXFP8 output: a 32-column block of the activation row is one MX block, held half by
       // this lane and half by lane ^ 32 (the same token row), which share its largest magnitude
@@ -437,7 +466,18 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
     } else if constexpr (EPI == EPI_BF16) {
       uint16_t* crow = (uint16_t*)p.c + (out_row0 + tok) * p.ldc;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        const int col0 = t.n_t * BN + wn * SH::WTN + j * 32;
+        if (col0 + 32 <= p.N) {  // a whole block (the lane pair of the token row agrees)
+#pragma unroll
+          for (int q = 0; q < 4; q += 2)
+            *(uint4*)(crow + col0 + 8 * q + 8 * hi) = swap_halves(
+                pack_bf16x2(scaled(i, j, q, 0), scaled(i, j, q, 1)),
+                pack_bf16x2(scaled(i, j, q, 2), scaled(i, j, q, 3)),
+                pack_bf16x2(scaled(i, j, q + 1, 0), scaled(i, j, q + 1, 1)),
+                pack_bf16x2(scaled(i, j, q + 1, 2), scaled(i, j, q + 1, 3)));
+          continue;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = t.n_t * BN + wn * SH::WTN + j * 32 + 8 * q + 4 * hi;
@@ -448,6 +488,7 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
             *(uint2*)(crow + col) = v;
           }
         }
+      }
     } else {
       float* crow = (float*)p.c + ks * p.c_split_stride + (out_row0 + tok) * p.ldc;
 #pragma unroll
