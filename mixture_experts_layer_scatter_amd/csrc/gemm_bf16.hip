@@ -457,10 +457,15 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileLoc& 
           }
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         const uint32_t sc = mxfp8_scale_code(amax);
+        uint32_t w[4];  // codes of columns 8q + 4hi .. + 3
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *(uint32_t*)(crow + col0 + 8 * q + 4 * hi) =
-              mxfp8_pack4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], sc);
+          w[q] = mxfp8_pack4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], sc);
+        // lane half 0 trades its quads 2, 3 (columns 16 .., 24 ..) for half 1's quads 0, 1
+        // (columns 4 .., 12 ..): half h then holds columns 16h .. 16h + 15, one 16-byte store
+        const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        *(uint4*)(crow + col0 + 16 * hi) = make_uint4(s02[0], s02[1], s13[0], s13[1]);
         if (hi == 0) srow[col0 / 32] = (uint8_t)sc;
       }
     } else if constexpr (EPI == EPI_BF16) {
