@@ -261,8 +261,9 @@ def measure(w, args, steps, warmup, cache_slots=0, weights=None):
     load["ms"] = round(e0.elapsed_ms(e1) / n_ls, 4)
 
     cache_res = None
-    if cache_slots > 0 and not lowbit:
-        cache_res = measure_cache(moe, d, t, cache_slots, ms_per_step, log)
+    if cache_slots > 0 and (not lowbit or a8):
+        cache_res = measure_cache(moe, d, t, cache_slots, ms_per_step, log,
+                                  mx=(q, q_sh) if a8 else None)
 
     es = 2 if w.dtype == "bf16" else 4
     # bytes of one expert weight element, and of the scales of a [rows, K] weight
@@ -366,19 +367,25 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measure_cache(moe, d, t, slots, uncached_ms, log):
+def measure_cache(moe, d, t, slots, uncached_ms, log, mx=None):
     """The layer with its routed experts in an HBM expert cache of `slots` slots, filled from
     pinned host memory: the first (cold) call loads every expert the batch needs over PCIe, the
     later (warm) calls find them resident.  Also times a plain pinned host-to-device copy of the
-    same bytes on the same copy stream, the PCIe reference."""
+    same bytes on the same copy stream, the PCIe reference.  mx = (codes and scales of w1, w3,
+    w2 by name, the shared expert's): an MXFP4 cache, the layer on MXFP8 activations."""
     import numpy as np
     import torch
     log(f"expert cache: {slots} slots, pinning host copies of the expert weights")
-    host = []
-    for k in ("w1", "w3", "w2"):
-        h = torch.empty(t[k].shape, dtype=t[k].dtype, pin_memory=True)
-        h.copy_(t[k])
-        host.append(h)
+
+    def pinned(a):
+        h = torch.empty(a.shape, dtype=a.dtype, pin_memory=True)
+        h.copy_(a)
+        return h
+
+    if mx is None:
+        host = [pinned(t[k]) for k in ("w1", "w3", "w2")]
+    else:
+        host = [tuple(pinned(a) for a in mx[0][k]) for k in ("w1", "w3", "w2")]
     cache = moe.ExpertCache(d, slots, *host)
     copy = torch.cuda.Stream()
     ws = moe.workspace(d)
@@ -387,8 +394,12 @@ def measure_cache(moe, d, t, slots, uncached_ms, log):
     def run():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        _, info = moe.layer_forward_cached(d, t["x"], t["wg"], t["bias"], cache, t["shared"], y=y,
-                                           ws=ws, copy_stream=copy)
+        if mx is None:
+            _, info = moe.layer_forward_cached(d, t["x"], t["wg"], t["bias"], cache, t["shared"],
+                                               y=y, ws=ws, copy_stream=copy)
+        else:
+            _, info = moe.layer_forward_cached_w4a8(d, t["x"], t["wg"], t["bias"], cache, mx[1],
+                                                    y=y, ws=ws, copy_stream=copy)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3, info
 

@@ -383,9 +383,13 @@ moe_status_t moe_layer_forward_w4a8(const moe_dims_t* dims, const void* x, const
  * far on the compute stream (which may still read those slots) and after
  * every earlier copy of this cache; the compute stream's later work waits for
  * every copy of this cache enqueued so far.  The copies thus run
- * asynchronously to the host and to other streams.  bf16 layers only.  The object holds host bookkeeping (allocated in moe_cache_create, freed
- * in moe_cache_destroy) and two HIP events; one object must not be used from
- * two threads at once. */
+ * asynchronously to the host and to other streams.  bf16 layers only.  A cache
+ * holds the experts either in bf16 (moe_cache_create) or as MXFP4 codes and
+ * scales (moe_cache_create_mxfp4: [P3] §5.2 serves with the expert cache and
+ * 4-bit experts together; a slot then costs about a quarter of the HBM and of
+ * the host -> device bytes).  The object holds host bookkeeping (allocated in
+ * moe_cache_create*, freed in moe_cache_destroy) and two HIP events; one object
+ * must not be used from two threads at once. */
 typedef struct moe_expert_cache moe_expert_cache_t;
 
 /* Outcome of one batch's residency request. */
@@ -408,6 +412,24 @@ size_t moe_cache_pool_bytes(const moe_dims_t* dims, int32_t slots);
 moe_status_t moe_cache_create(const moe_dims_t* dims, int32_t slots, const void* host_w1,
                               const void* host_w3, const void* host_w2, void* pool,
                               size_t pool_bytes, moe_expert_cache_t** cache);
+
+/* Device bytes of a pool of `slots` MXFP4 expert slots (codes, scales) plus
+ * the table (0 on invalid dims, slots < 1, or H, I not multiples of 128). */
+size_t moe_cache_pool_bytes_mxfp4(const moe_dims_t* dims, int32_t slots);
+
+/* An expert cache of MXFP4 experts: host_w1q/host_w1s and host_w3q/host_w3s
+ * as moe_quantize_mxfp4 writes [E*I, H], host_w2q/host_w2s as it writes
+ * [E*H, I] (host memory, pinned for asynchronous copies, owned by the caller
+ * and kept alive as long as the cache); pool: device memory of at least
+ * moe_cache_pool_bytes_mxfp4.  dims->dtype must be MOE_BF16 and H, I
+ * multiples of 128 (else MOE_ERR_UNSUPPORTED).  Used by
+ * moe_layer_forward_cached_w4a8; moe_cache_load and moe_cache_slots work on
+ * it as on a bf16 cache (bytes_loaded counts codes and scales). */
+moe_status_t moe_cache_create_mxfp4(const moe_dims_t* dims, int32_t slots,
+                                    const uint8_t* host_w1q, const uint8_t* host_w1s,
+                                    const uint8_t* host_w3q, const uint8_t* host_w3s,
+                                    const uint8_t* host_w2q, const uint8_t* host_w2s, void* pool,
+                                    size_t pool_bytes, moe_expert_cache_t** cache);
 void moe_cache_destroy(moe_expert_cache_t* cache);
 
 /* Make the n experts in `experts` (host array, ids in [0, E), duplicates
@@ -436,6 +458,22 @@ moe_status_t moe_layer_forward_cached(const moe_dims_t* dims, const void* x, con
                                       const void* ws1, const void* ws3, const void* ws2, void* y,
                                       const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
                                       void* stream, void* copy_stream, moe_cache_step_t* info);
+
+/* moe_layer_forward_cached on an MXFP4 expert cache (moe_cache_create_mxfp4),
+ * computing as moe_layer_forward_w4a8: MXFP8 activations on the cached MXFP4
+ * experts; the shared expert's MXFP4 weights (ws1q/ws1s, ... as in
+ * moe_layer_forward_w4a8) are not cached.  The output is bit for bit that of
+ * moe_layer_forward_w4a8 with the same codes and scales.  A bf16 cache, or an
+ * MXFP4 cache passed to moe_layer_forward_cached, is MOE_ERR_INVALID_ARG.
+ * Same waits and failure modes as moe_layer_forward_cached. */
+moe_status_t moe_layer_forward_cached_w4a8(const moe_dims_t* dims, const void* x, const void* wg,
+                                           const float* bias, moe_expert_cache_t* cache,
+                                           const uint8_t* ws1q, const uint8_t* ws1s,
+                                           const uint8_t* ws3q, const uint8_t* ws3s,
+                                           const uint8_t* ws2q, const uint8_t* ws2s, void* y,
+                                           const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                           void* stream, void* copy_stream,
+                                           moe_cache_step_t* info);
 
 /* The whole layer in one enqueue: gate, route (+bias, capacity), permute,
  * grouped gate-up with SiLU*mul, grouped down, combine.  The pack is fused into

@@ -10,4 +10,4 @@ from .api import (Dims, ExpertCache, capacity, combine, expert_ffn, expert_ffn_f
                   layer_forward_mxfp4, load_stats, load_stats_buffer, permute, quantize_fp8,
                   quantize_mxfp4, read_load_stats, route, workspace, workspace_bytes,
                   layer_forward_static, static_scratch_bytes, quantize_mxfp8, expert_ffn_w4a8,
-                  layer_forward_w4a8)
+                  layer_forward_w4a8, layer_forward_cached_w4a8)

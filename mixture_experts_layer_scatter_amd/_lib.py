@@ -18,7 +18,8 @@ EXPORTS = ("moe_status_str", "moe_capacity", "moe_workspace_bytes", "moe_gate", 
            "moe_layer_forward_mxfp4", "moe_cache_pool_bytes", "moe_cache_create", "moe_cache_destroy",
            "moe_cache_load", "moe_cache_slots", "moe_layer_forward", "moe_layer_forward_fp8",
            "moe_layer_forward_cached", "moe_static_scratch_bytes", "moe_layer_forward_static",
-           "moe_quantize_mxfp8", "moe_expert_ffn_w4a8", "moe_layer_forward_w4a8")
+           "moe_quantize_mxfp8", "moe_expert_ffn_w4a8", "moe_layer_forward_w4a8",
+           "moe_cache_pool_bytes_mxfp4", "moe_cache_create_mxfp4", "moe_layer_forward_cached_w4a8")
 MOE_BIAS_SOFTMAX, MOE_BIAS_SELECT = 0, 1
 
 
@@ -104,6 +105,13 @@ def lib():
         L.moe_expert_ffn_w4a8.argtypes = [D, p, p, p, p, p, p, p, p, p, p, sz, p]
         L.moe_layer_forward_w4a8.restype = i32
         L.moe_layer_forward_w4a8.argtypes = [D] + [p] * 16 + [C.POINTER(MoeDebugOut), p, sz, p]
+        L.moe_cache_pool_bytes_mxfp4.restype = sz
+        L.moe_cache_pool_bytes_mxfp4.argtypes = [D, i32]
+        L.moe_cache_create_mxfp4.restype = i32
+        L.moe_cache_create_mxfp4.argtypes = [D, i32, p, p, p, p, p, p, p, sz, C.POINTER(p)]
+        L.moe_layer_forward_cached_w4a8.restype = i32
+        L.moe_layer_forward_cached_w4a8.argtypes = [D, p, p, p, p] + [p] * 7 + [
+            C.POINTER(MoeDebugOut), p, sz, p, p, C.POINTER(MoeCacheStep)]
         L.moe_cache_pool_bytes.restype = sz
         L.moe_cache_pool_bytes.argtypes = [D, i32]
         L.moe_cache_create.restype = i32

@@ -330,20 +330,31 @@ class ExpertCache:
     them for asynchronous copies).  The host tensors must outlive the cache."""
 
     def __init__(self, d: Dims, slots: int, w1, w3, w2, device="cuda"):
-        for name, t in (("w1", w1), ("w3", w3), ("w2", w2)):
-            if t.is_cuda or t.dtype != d.torch_dtype or not t.is_contiguous():
-                raise ValueError(f"{name}: contiguous host tensor of {d.torch_dtype} expected")
-        self._keep = (w1, w3, w2)
+        """w1, w3, w2: bf16 host tensors, or (for an MXFP4 cache) (codes, scales) pairs of uint8
+        host tensors as quantize_mxfp4 returns them for [E, I, H] and [E, H, I]."""
+        self.mxfp4 = isinstance(w1, tuple)
+        parts = [a for w in (w1, w3, w2) for a in (w if self.mxfp4 else (w,))]
+        want = torch.uint8 if self.mxfp4 else d.torch_dtype
+        for t in parts:
+            if t.is_cuda or t.dtype != want or not t.is_contiguous():
+                raise ValueError(f"expert weights: contiguous host tensors of {want} expected")
+        self._keep = parts
         self.d = d
         c = d.c()
-        n = int(_lib.lib().moe_cache_pool_bytes(C.byref(c), slots))
+        L = _lib.lib()
+        pool_bytes = L.moe_cache_pool_bytes_mxfp4 if self.mxfp4 else L.moe_cache_pool_bytes
+        n = int(pool_bytes(C.byref(c), slots))
         if n == 0:
             raise ValueError(f"invalid cache dims {d} / slots {slots}")
         self.pool = torch.empty(n, dtype=torch.uint8, device=device)
         h = C.c_void_p()
-        _check(_lib.lib().moe_cache_create(C.byref(c), slots, w1.data_ptr(), w3.data_ptr(),
-                                           w2.data_ptr(), self.pool.data_ptr(), n, C.byref(h)),
-               "moe_cache_create")
+        ptrs = [t.data_ptr() for t in parts]
+        if self.mxfp4:
+            _check(L.moe_cache_create_mxfp4(C.byref(c), slots, *ptrs, self.pool.data_ptr(), n,
+                                            C.byref(h)), "moe_cache_create_mxfp4")
+        else:
+            _check(L.moe_cache_create(C.byref(c), slots, *ptrs, self.pool.data_ptr(), n,
+                                      C.byref(h)), "moe_cache_create")
         self.handle = h
 
     def load(self, experts, copy_stream=None, stream=None) -> dict:
@@ -391,6 +402,32 @@ def layer_forward_cached(d: Dims, x, wg, bias, cache: ExpertCache, shared=None, 
         C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream), _stream(copy_stream if copy_stream is not None else stream),
         C.byref(info)), "moe_layer_forward_cached")
+    return y, _step_dict(info)
+
+
+def layer_forward_cached_w4a8(d: Dims, x, wg, bias, cache: ExpertCache, shared=None, y=None,
+                              ws=None, debug=None, stream=None, copy_stream=None):
+    """The fused layer on MXFP8 activations with the routed experts' MXFP4 weights in an MXFP4
+    ExpertCache; shared: the shared expert's (codes, scales) pairs on the device, or None.
+    Returns (y, step info)."""
+    dt = d.torch_dtype
+    if y is None:
+        y = torch.empty((d.T, d.H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(d, x.device)
+    none = (None, None)
+    (e1, t1), (e3, t3), (e2, t2) = shared if shared is not None else (none, none, none)
+    u8 = torch.uint8
+    dbg = _debug_struct(debug) if debug else None
+    info = MoeCacheStep()
+    c = d.c()
+    _check(_lib.lib().moe_layer_forward_cached_w4a8(
+        C.byref(c), _ptr(x, dt, "x"), _ptr(wg, dt, "wg"), _ptr(bias, torch.float32, "bias"),
+        cache.handle, _ptr(e1, u8, "ws1q"), _ptr(t1, u8, "ws1s"), _ptr(e3, u8, "ws3q"),
+        _ptr(t3, u8, "ws3s"), _ptr(e2, u8, "ws2q"), _ptr(t2, u8, "ws2s"), _ptr(y, dt, "y"),
+        C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream), _stream(copy_stream if copy_stream is not None else stream),
+        C.byref(info)), "moe_layer_forward_cached_w4a8")
     return y, _step_dict(info)
 
 

@@ -582,6 +582,7 @@ struct CacheUse {
   moe_expert_cache_t* cache;
   hipStream_t copy_stream;
   moe_cache_step_t* info;
+  bool a8;  // MXFP4 experts on MXFP8 activations: the cache must hold MXFP4 codes and scales
 };
 
 moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* wg,
@@ -597,7 +598,8 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
     if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     const CacheView v = cache_view(cu->cache);
     if (v.E != d->E || v.H != d->H || v.I != d->I) return MOE_ERR_INVALID_ARG;
-    W = plain_weights(v.w1, v.w3, v.w2);
+    if (v.mx != cu->a8) return MOE_ERR_INVALID_ARG;  // the cache's format is the entry point's
+    W = v.mx ? w4a8_weights(v.w1, v.s1, v.w3, v.s3, v.w2, v.s2) : plain_weights(v.w1, v.w3, v.w2);
     group_slot = v.table;
   }
   if (!x || !wg || !W.complete() || !y) {
@@ -727,9 +729,26 @@ moe_status_t moe_layer_forward_cached(const moe_dims_t* d, const void* x, const 
                                       void* stream, void* copy_stream, moe_cache_step_t* info) {
   if (!cache) return MOE_ERR_INVALID_ARG;
   if (info) *info = moe_cache_step_t{};
-  const CacheUse cu{cache, (hipStream_t)copy_stream, info};
+  const CacheUse cu{cache, (hipStream_t)copy_stream, info, false};
   return layer_forward_impl(d, x, wg, bias, ExpertWeights{},
                             plain_weights(ws1, ws3, ws2), y, dbg, ws,
+                            ws_bytes, stream, &cu);
+}
+
+moe_status_t moe_layer_forward_cached_w4a8(const moe_dims_t* d, const void* x, const void* wg,
+                                           const float* bias, moe_expert_cache_t* cache,
+                                           const uint8_t* ws1q, const uint8_t* ws1s,
+                                           const uint8_t* ws3q, const uint8_t* ws3s,
+                                           const uint8_t* ws2q, const uint8_t* ws2s, void* y,
+                                           const moe_debug_out_t* dbg, void* ws, size_t ws_bytes,
+                                           void* stream, void* copy_stream,
+                                           moe_cache_step_t* info) {
+  if (!cache) return MOE_ERR_INVALID_ARG;
+  if (info) *info = moe_cache_step_t{};
+  if (d && d->I_shared > 0 && (!ws1s || !ws3s || !ws2s)) return MOE_ERR_INVALID_ARG;
+  const CacheUse cu{cache, (hipStream_t)copy_stream, info, true};
+  return layer_forward_impl(d, x, wg, bias, ExpertWeights{},
+                            w4a8_weights(ws1q, ws1s, ws3q, ws3s, ws2q, ws2s), y, dbg, ws,
                             ws_bytes, stream, &cu);
 }
 

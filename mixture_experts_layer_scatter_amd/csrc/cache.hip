@@ -4,7 +4,9 @@
 // subset of the experts in HBM and loads the others from host memory before a
 // batch needs them, evicting the least recently used, with the copies on a
 // separate stream so they can overlap compute.  Here the pool (W1, W3, W2 per
-// slot, and the device expert -> slot table) is caller-allocated device memory;
+// slot, and the device expert -> slot table) is caller-allocated device memory, holding the
+// experts in the layer's bf16 or as MXFP4 codes and scales (§5.2 of the same page serves with
+// the expert cache and 4-bit experts together, so a slot then costs a quarter of the bytes);
 // this file holds the host-side residency bookkeeping, the copies and the
 // table updates.  The grouped GEMMs read expert e's weights from slot table[e]
 // (GroupedGemm::group_slot).
@@ -24,29 +26,39 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Pool: W1, W3, W2 slots (bf16 values or MXFP4 codes), then (MXFP4) their scale slots, then
+// the table.  An MXFP4 expert's codes and scales are each one contiguous block, as
+// moe_quantize_mxfp4 writes them for [E * I, H] and [E * H, I].
 struct PoolLayout {
-  size_t w1, w3, w2, table, total, expert_bytes_13, expert_bytes_2;
+  size_t w1, w3, w2, s1, s3, s2, table, total;
+  size_t code_13, code_2, scale_13, scale_2;  // bytes of one expert
 };
 
-bool cache_dims_ok(const moe_dims_t* d) {
-  return d && d->H > 0 && d->E > 0 && d->E <= moe::kMaxExperts && d->I > 0 &&
-         d->dtype == MOE_BF16 && d->H % 64 == 0 && d->I % 64 == 0;
+bool cache_dims_ok(const moe_dims_t* d, bool mx) {
+  if (!d || d->H <= 0 || d->E <= 0 || d->E > moe::kMaxExperts || d->I <= 0 ||
+      d->dtype != MOE_BF16)
+    return false;
+  return mx ? d->H % 128 == 0 && d->I % 128 == 0 : d->H % 64 == 0 && d->I % 64 == 0;
 }
 
-PoolLayout pool_layout(const moe_dims_t* d, int slots) {
+PoolLayout pool_layout(const moe_dims_t* d, int slots, bool mx) {
   PoolLayout L;
-  const size_t es = 2;
-  L.expert_bytes_13 = (size_t)d->I * d->H * es;
-  L.expert_bytes_2 = (size_t)d->H * d->I * es;
+  const size_t n = (size_t)d->I * d->H;
+  L.code_13 = L.code_2 = mx ? n / 2 : n * 2;
+  L.scale_13 = L.scale_2 = mx ? n / 32 : 0;
   size_t o = 0;
-  L.w1 = o;
-  o += align_up((size_t)slots * L.expert_bytes_13);
-  L.w3 = o;
-  o += align_up((size_t)slots * L.expert_bytes_13);
-  L.w2 = o;
-  o += align_up((size_t)slots * L.expert_bytes_2);
-  L.table = o;
-  o += align_up((size_t)d->E * 4);
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.w1 = take((size_t)slots * L.code_13);
+  L.w3 = take((size_t)slots * L.code_13);
+  L.w2 = take((size_t)slots * L.code_2);
+  L.s1 = take((size_t)slots * L.scale_13);
+  L.s3 = take((size_t)slots * L.scale_13);
+  L.s2 = take((size_t)slots * L.scale_2);
+  L.table = take((size_t)d->E * 4);
   L.total = o;
   return L;
 }
@@ -70,10 +82,11 @@ __global__ __launch_bounds__(256) void cache_table_kernel(int32_t* table, TableU
 
 struct moe_expert_cache {
   int E, H, I, slots;
-  const char *hw1, *hw3, *hw2;
-  char *pw1, *pw3, *pw2;
+  bool mx;  // MXFP4 codes and scales (else bf16 values)
+  const char *hw1, *hw3, *hw2, *hs1, *hs3, *hs2;
+  char *pw1, *pw3, *pw2, *ps1, *ps3, *ps2;
   int32_t* table;
-  size_t bytes13, bytes2;
+  size_t bytes13, bytes2, sbytes13, sbytes2;
   std::vector<int32_t> slot_of, expert_in;
   std::vector<int64_t> last_use;
   int64_t step;
@@ -89,6 +102,10 @@ CacheView cache_view(const moe_expert_cache* c) {
   v.w1 = c->pw1;
   v.w3 = c->pw3;
   v.w2 = c->pw2;
+  v.s1 = (const uint8_t*)c->ps1;
+  v.s3 = (const uint8_t*)c->ps3;
+  v.s2 = (const uint8_t*)c->ps2;
+  v.mx = c->mx;
   v.table = c->table;
   v.E = c->E;
   v.H = c->H;
@@ -101,18 +118,29 @@ CacheView cache_view(const moe_expert_cache* c) {
 extern "C" {
 
 size_t moe_cache_pool_bytes(const moe_dims_t* d, int32_t slots) {
-  if (!cache_dims_ok(d) || slots < 1) return 0;
-  return pool_layout(d, slots).total;
+  if (!cache_dims_ok(d, false) || slots < 1) return 0;
+  return pool_layout(d, slots, false).total;
 }
 
-moe_status_t moe_cache_create(const moe_dims_t* d, int32_t slots, const void* host_w1,
-                              const void* host_w3, const void* host_w2, void* pool,
-                              size_t pool_bytes, moe_expert_cache_t** out) {
+size_t moe_cache_pool_bytes_mxfp4(const moe_dims_t* d, int32_t slots) {
+  if (!cache_dims_ok(d, true) || slots < 1) return 0;
+  return pool_layout(d, slots, true).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// host arrays: w = the values (bf16) or codes (MXFP4), s = the MXFP4 scales (null for bf16)
+moe_status_t cache_create(const moe_dims_t* d, int32_t slots, bool mx, const void* const w[3],
+                          const void* const sc[3], void* pool, size_t pool_bytes,
+                          moe_expert_cache_t** out) {
   if (!out) return MOE_ERR_INVALID_ARG;
   *out = nullptr;
-  if (!d || slots < 1 || !host_w1 || !host_w3 || !host_w2 || !pool) return MOE_ERR_INVALID_ARG;
-  if (!cache_dims_ok(d)) return MOE_ERR_UNSUPPORTED;
-  const PoolLayout L = pool_layout(d, slots);
+  if (!d || slots < 1 || !w[0] || !w[1] || !w[2] || !pool) return MOE_ERR_INVALID_ARG;
+  if (mx && (!sc[0] || !sc[1] || !sc[2])) return MOE_ERR_INVALID_ARG;
+  if (!cache_dims_ok(d, mx)) return MOE_ERR_UNSUPPORTED;
+  const PoolLayout L = pool_layout(d, slots, mx);
   if (pool_bytes < L.total) return MOE_ERR_WORKSPACE;
   moe_expert_cache* c = new (std::nothrow) moe_expert_cache();
   if (!c) return MOE_ERR_HIP;
@@ -120,15 +148,24 @@ moe_status_t moe_cache_create(const moe_dims_t* d, int32_t slots, const void* ho
   c->H = d->H;
   c->I = d->I;
   c->slots = slots;
-  c->hw1 = (const char*)host_w1;
-  c->hw3 = (const char*)host_w3;
-  c->hw2 = (const char*)host_w2;
+  c->mx = mx;
+  c->hw1 = (const char*)w[0];
+  c->hw3 = (const char*)w[1];
+  c->hw2 = (const char*)w[2];
+  c->hs1 = (const char*)sc[0];
+  c->hs3 = (const char*)sc[1];
+  c->hs2 = (const char*)sc[2];
   c->pw1 = (char*)pool + L.w1;
   c->pw3 = (char*)pool + L.w3;
   c->pw2 = (char*)pool + L.w2;
+  c->ps1 = mx ? (char*)pool + L.s1 : nullptr;
+  c->ps3 = mx ? (char*)pool + L.s3 : nullptr;
+  c->ps2 = mx ? (char*)pool + L.s2 : nullptr;
   c->table = (int32_t*)((char*)pool + L.table);
-  c->bytes13 = L.expert_bytes_13;
-  c->bytes2 = L.expert_bytes_2;
+  c->bytes13 = L.code_13;
+  c->bytes2 = L.code_2;
+  c->sbytes13 = L.scale_13;
+  c->sbytes2 = L.scale_2;
   c->slot_of.assign(d->E, -1);
   c->expert_in.assign(slots, -1);
   c->last_use.assign(d->E, -1);
@@ -146,6 +183,28 @@ moe_status_t moe_cache_create(const moe_dims_t* d, int32_t slots, const void* ho
   }
   *out = c;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_cache_create(const moe_dims_t* d, int32_t slots, const void* host_w1,
+                              const void* host_w3, const void* host_w2, void* pool,
+                              size_t pool_bytes, moe_expert_cache_t** out) {
+  const void* w[3] = {host_w1, host_w3, host_w2};
+  const void* sc[3] = {nullptr, nullptr, nullptr};
+  return cache_create(d, slots, false, w, sc, pool, pool_bytes, out);
+}
+
+moe_status_t moe_cache_create_mxfp4(const moe_dims_t* d, int32_t slots, const uint8_t* host_w1q,
+                                    const uint8_t* host_w1s, const uint8_t* host_w3q,
+                                    const uint8_t* host_w3s, const uint8_t* host_w2q,
+                                    const uint8_t* host_w2s, void* pool, size_t pool_bytes,
+                                    moe_expert_cache_t** out) {
+  const void* w[3] = {host_w1q, host_w3q, host_w2q};
+  const void* sc[3] = {host_w1s, host_w3s, host_w2s};
+  return cache_create(d, slots, true, w, sc, pool, pool_bytes, out);
 }
 
 void moe_cache_destroy(moe_expert_cache_t* c) {
@@ -233,6 +292,14 @@ moe_status_t moe_cache_load(moe_expert_cache_t* c, const int32_t* experts, int32
           hipMemcpyAsync(c->pw2 + (size_t)s * c->bytes2, c->hw2 + (size_t)e * c->bytes2,
                          c->bytes2, hipMemcpyHostToDevice, cs) != hipSuccess)
         return MOE_ERR_HIP;
+      if (c->mx &&
+          (hipMemcpyAsync(c->ps1 + (size_t)s * c->sbytes13, c->hs1 + (size_t)e * c->sbytes13,
+                          c->sbytes13, hipMemcpyHostToDevice, cs) != hipSuccess ||
+           hipMemcpyAsync(c->ps3 + (size_t)s * c->sbytes13, c->hs3 + (size_t)e * c->sbytes13,
+                          c->sbytes13, hipMemcpyHostToDevice, cs) != hipSuccess ||
+           hipMemcpyAsync(c->ps2 + (size_t)s * c->sbytes2, c->hs2 + (size_t)e * c->sbytes2,
+                          c->sbytes2, hipMemcpyHostToDevice, cs) != hipSuccess))
+        return MOE_ERR_HIP;
     }
     if (hipEventRecord(c->ev_copies, cs) != hipSuccess) return MOE_ERR_HIP;
     c->copies_issued = true;
@@ -265,7 +332,8 @@ moe_status_t moe_cache_load(moe_expert_cache_t* c, const int32_t* experts, int32
     info->hits = hits;
     info->loads = (int32_t)placed.size();
     info->evictions = evictions;
-    info->bytes_loaded = (int64_t)placed.size() * (int64_t)(2 * c->bytes13 + c->bytes2);
+    info->bytes_loaded = (int64_t)placed.size() *
+                         (int64_t)(2 * c->bytes13 + c->bytes2 + 2 * c->sbytes13 + c->sbytes2);
   }
   return MOE_OK;
 }

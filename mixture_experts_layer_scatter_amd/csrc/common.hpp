@@ -177,7 +177,9 @@ size_t gemm_tail_bytes(int avg_rows_per_group);
 
 // cache.hip: the device side of an expert cache (pool slots and the expert -> slot table)
 struct CacheView {
-  const void *w1, *w3, *w2;  // [slots, I, H], [slots, I, H], [slots, H, I]
+  const void *w1, *w3, *w2;  // [slots, I, H], [slots, I, H], [slots, H, I] (values or codes)
+  const uint8_t *s1, *s3, *s2;  // MXFP4: the slots' E8M0 scales; else null
+  bool mx;
   const int32_t* table;      // [E] expert -> slot
   int E, H, I;
 };

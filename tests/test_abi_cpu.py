@@ -207,6 +207,37 @@ def test_cache_argument_checks():
                                         p, 1 << 40, None, None, None) == L.MOE_ERR_INVALID_ARG
 
 
+def test_mxfp4_cache_argument_checks():
+    """An MXFP4 expert cache: its pool is about a quarter of the bf16 one's (codes, a scale
+    byte per 32, the table), it takes H and I in 128s, and every argument is checked before
+    any device call."""
+    L = _lib()
+    lib = L.lib()
+    p = C.c_void_p(16)  # never dereferenced
+    d = _dims(E=8, H=256, I=128)
+    n = lib.moe_cache_pool_bytes_mxfp4(C.byref(d), 4)
+    per_slot = 3 * 128 * 256 // 2 + 3 * 128 * 256 // 32
+    assert n >= 4 * per_slot and n % 256 == 0
+    assert n < lib.moe_cache_pool_bytes(C.byref(d), 4) // 3
+    assert lib.moe_cache_pool_bytes_mxfp4(C.byref(_dims(H=192)), 4) == 0
+    assert lib.moe_cache_pool_bytes_mxfp4(C.byref(d), 0) == 0
+    out = C.c_void_p(123)
+    args = [p] * 6
+    assert lib.moe_cache_create_mxfp4(C.byref(d), 4, *args, p, n, None) == L.MOE_ERR_INVALID_ARG
+    for i in range(6):  # every code and scale array is needed
+        a = list(args)
+        a[i] = None
+        assert lib.moe_cache_create_mxfp4(C.byref(d), 4, *a, p, n, C.byref(out)) == \
+            L.MOE_ERR_INVALID_ARG, i
+        assert out.value is None
+    assert lib.moe_cache_create_mxfp4(C.byref(d), 4, *args, p, n - 1, C.byref(out)) == \
+        L.MOE_ERR_WORKSPACE
+    assert lib.moe_cache_create_mxfp4(C.byref(_dims(H=192)), 4, *args, p, 1 << 40, C.byref(out)) == \
+        L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_forward_cached_w4a8(C.byref(d), p, p, None, None, *([None] * 6), p, None,
+                                             p, 1 << 40, None, None, None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_mxfp4_entry_point_checks():
     L = _lib()
     lib = L.lib()

@@ -145,3 +145,131 @@ def _pinned_from(t):
     h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
     h.copy_(t)
     return h
+
+
+# ---- MXFP4 expert cache, computing with MXFP8 activations -------------------------------------
+
+def _pinned_u8(t):
+    h = torch.empty(t.shape, dtype=torch.uint8, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+def _mx_host(W):
+    """bf16 weights [E, R, K] -> their MXFP4 (codes, scales) on the device and pinned host copies."""
+    q, s = moe.quantize_mxfp4(dev(W))
+    torch.cuda.synchronize()
+    return (q, s), (_pinned_u8(q.cpu()), _pinned_u8(s.cpu()))
+
+
+@pytest.mark.parametrize("E,slots", [(16, 5), (48, 20)])
+def test_mxfp4_cache_residency_and_slots(E, slots):
+    """The MXFP4 cache follows the same LRU model, loads codes and scales (bytes_loaded counts
+    both), and each resident slot holds its expert's codes and scales bit for bit."""
+    need_gpu()
+    log(f"mxfp4 cache residency E={E} slots={slots}")
+    rng = np.random.default_rng(E + 1)
+    H, I = 256, 128
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    dq = [_mx_host(W) for W in (W1, W3, W2)]
+    d = moe.Dims(T=1, H=H, E=E, k=1, I=I)
+    cache = moe.ExpertCache(d, slots, dq[0][1], dq[1][1], dq[2][1])
+    ref = LRUCache(E, slots)
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+    p /= p.sum()
+    copy = torch.cuda.Stream()
+    per_expert = 3 * (H * I // 2 + H * I // 32)
+    for step in range(40):
+        req = rng.choice(E, int(rng.integers(1, slots + 1)), replace=False, p=p).tolist()
+        info = cache.load(req, copy_stream=copy)
+        hits, loads, ev = ref.request(req)
+        assert (info["hits"], info["loads"], info["evictions"]) == (len(hits), len(loads), len(ev)), step
+        assert info["bytes_loaded"] == len(loads) * per_expert
+        assert cache.slots().tolist() == ref.slot_of, step
+    torch.cuda.synchronize()
+    # pool: W1, W3, W2 code slots, then their scale slots (each region 256-byte aligned)
+    pool = cache.pool
+    nc, ns = slots * I * H // 2, slots * I * H // 32
+    off = [0]
+    for n in (nc, nc, nc, ns, ns, ns):
+        off.append(off[-1] + _align(n))
+    views = [pool[off[i]:off[i] + (nc if i < 3 else ns)].view(slots, -1) for i in range(6)]
+    host = [dq[0][1][0], dq[1][1][0], dq[2][1][0], dq[0][1][1], dq[1][1][1], dq[2][1][1]]
+    for e, s in enumerate(cache.slots()):
+        if s >= 0:
+            for v, h in zip(views, host):
+                assert torch.equal(v[s].cpu(), h[e].reshape(-1)), (e, s)
+    cache.close()
+
+
+@pytest.mark.parametrize("E,slots,T,k,shared", [(16, 6, 3, 2, 0), (32, 10, 5, 2, 256)])
+def test_cached_w4a8_layer_bit_exact(E, slots, T, k, shared):
+    """moe_layer_forward_cached_w4a8 equals moe_layer_forward_w4a8 on the same codes and scales
+    bit for bit, batch after batch, with evictions."""
+    need_gpu()
+    log(f"cached w4a8 layer E={E} slots={slots} T={T} k={k} shared={shared}")
+    rng = np.random.default_rng(E * 11 + T)
+    H, I = 256, 128
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    dq = [_mx_host(W) for W in (W1, W3, W2)]
+    wg = bf16_normal(rng, (E, H), 1 / np.sqrt(H))
+    bias = (-0.5 * np.log(rng.permutation(E) + 1.0)).astype(np.float32)
+    d = moe.Dims(T=T, H=H, E=E, k=k, I=I, I_shared=shared)
+    sh = None
+    if shared:
+        sh = tuple(moe.quantize_mxfp4(dev(a)) for a in (
+            bf16_normal(rng, (shared, H), 1 / np.sqrt(H)), bf16_normal(rng, (shared, H), 1 / np.sqrt(H)),
+            bf16_normal(rng, (H, shared), 1 / np.sqrt(shared))))
+    cache = moe.ExpertCache(d, slots, dq[0][1], dq[1][1], dq[2][1])
+    dwg, dbias = dev(wg), dev(bias)
+    ref = LRUCache(E, slots)
+    copy = torch.cuda.Stream()
+    ws = moe.workspace(d)
+    total = dict(hits=0, loads=0, evictions=0)
+    for step in range(12):
+        x = dev(bf16_normal(rng, (T, H)))
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        y_ref = moe.layer_forward_w4a8(d, x, dwg, dbias, dq[0][0], dq[1][0], dq[2][0], sh, ws=ws)
+        y, info = moe.layer_forward_cached_w4a8(d, x, dwg, dbias, cache, sh, ws=ws,
+                                                debug=dict(counts=counts), copy_stream=copy)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), bits(y_ref)), step
+        need = np.nonzero(counts.cpu().numpy())[0].tolist()
+        hits, loads, ev = ref.request(need)
+        assert (info["hits"], info["loads"], info["evictions"]) == (len(hits), len(loads), len(ev))
+        for key in total:
+            total[key] += info[key]
+    log(f"  over 12 batches: {total}")
+    assert total["evictions"] > 0 and total["hits"] > 0
+    # the format of a cache is the entry point's
+    with pytest.raises(moe.MoeError):
+        moe.layer_forward_cached(d, x, dwg, dbias, cache, None, ws=ws, copy_stream=copy)
+    cache.close()
+
+
+def test_cached_w4a8_layer_against_oracle():
+    """One cached W4A8 layer call checked straight against the oracle's MXFP8 FFN on the same
+    MXFP4 codes dequantised, every token."""
+    need_gpu()
+    import oracle
+    from layer_check import check_against_oracle, run_layer
+    from moe_synth.device import workload_tensors
+    from oracle_steps import Mxfp4Weights
+    w = moe_synth.Workload("cache_oracle_w4a8", 211, T=200, H=256, E=16, k=2, I=128, zipf_s=1.2)
+    t = workload_tensors(w)
+    d = moe.Dims(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
+    host = []
+    for key in ("w1", "w3", "w2"):
+        q, s = moe.quantize_mxfp4(t[key])
+        host.append((_pinned_u8(q.cpu()), _pinned_u8(s.cpu())))
+    torch.cuda.synchronize()
+    cache = moe.ExpertCache(d, w.E, *host)
+    copy = torch.cuda.Stream()
+    cache.load([11, 3, 7], copy_stream=copy)
+    g = run_layer(w, lambda dd, dbg: moe.layer_forward_cached_w4a8(
+        dd, t["x"], t["wg"], t["bias"], cache, None, debug=dbg, copy_stream=copy)[0])
+    slot_of = cache.slots().tolist()
+    cache.close()
+    assert any(s >= 0 and s != e for e, s in enumerate(slot_of))
+    check_against_oracle(w, g, Mxfp4Weights(w, cache=False), None, tag=" (cached w4a8)",
+                         ffn=oracle.expert_ffn_a8)
