@@ -20,11 +20,11 @@
  *    `ws_bytes`), sized by moe_workspace_bytes().
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work and return; outputs are ready when the stream reaches that point.
- *    No call synchronises with the host, with one exception:
- *    moe_layer_forward_cached waits for `stream` in the middle of the call to
- *    read the per-expert row counts back (so it cannot be captured into a HIP
- *    graph).  The cache's bookkeeping calls (moe_cache_create, _destroy,
- *    _slots) are host-only.
+ *    No call synchronises with the host, except the expert cache's reports:
+ *    moe_cache_slots and moe_cache_last_step wait for the cache's last
+ *    residency step, and moe_cache_load, moe_layer_forward_cached and
+ *    moe_layer_forward_cached_w4a8 do so at their end when given a non-NULL
+ *    `info` to fill.
  *  - Device arrays start on 16-byte boundaries (hipMalloc and torch's
  *    allocator give 256): the kernels move rows with 16-byte vector accesses.
  *  - Layouts are row-major and contiguous.  Weights use the [out, in] layout
@@ -34,12 +34,13 @@
  *    packed rows and y.  Accumulation is always fp32; logits and routing
  *    weights are always fp32; ids, counts, offsets and positions are int32.
  *  - Arguments are checked on the host before anything is launched.  On error
- *    nothing is launched and outputs are untouched, with one exception:
- *    moe_layer_forward_cached learns how many distinct experts a batch needs
- *    only after its gate, route and permute have run, so it can return
- *    MOE_ERR_UNSUPPORTED (more experts than cache slots) or a copy error after
- *    enqueuing those steps; its outputs are then unspecified and the cache
- *    unchanged.  No C++ exception crosses the ABI.  T = 0 is a valid no-op.
+ *    nothing is launched and outputs are untouched, with one exception: the
+ *    cached layer learns how many distinct experts a batch needs only on the
+ *    device, after its routing; a batch that needs more than the cache has
+ *    slots leaves the cache unchanged, its outputs are unspecified, and the
+ *    call (with `info`) or a later moe_cache_last_step reports
+ *    MOE_ERR_UNSUPPORTED.  No C++ exception crosses the ABI.  T = 0 is a
+ *    valid no-op.
  *  - Deterministic: identical inputs give bitwise-identical outputs (no
  *    floating-point atomics; every sum has a fixed order).
  *  - Thread-safe: the library holds no mutable global state.
@@ -376,14 +377,17 @@ moe_status_t moe_layer_forward_w4a8(const moe_dims_t* dims, const void* x, const
  * device table expert -> slot, managed by a host-side object.  Residency
  * policy (readings): recency = the last batch that requested an expert (ties:
  * lower id); a batch's own experts are never evicted for it; free slots are
- * taken lowest first; missing experts load in ascending id order.
- * Loads are hipMemcpyAsync host -> device on a copy stream (the host weights
- * should be pinned, e.g. hipHostMalloc, for the copies to be asynchronous).
- * Ordering: the copies into evicted slots start after the work enqueued so
- * far on the compute stream (which may still read those slots) and after
- * every earlier copy of this cache; the compute stream's later work waits for
- * every copy of this cache enqueued so far.  The copies thus run
- * asynchronously to the host and to other streams.  bf16 layers only.  A cache
+ * taken lowest first; missing experts load in ascending id order; a batch
+ * that needs more distinct experts than there are slots changes nothing.
+ * Residency is decided on the device (one small kernel, from a host list or
+ * from the per-expert row counts a layer's routing left on the device), and a
+ * copy kernel reads the missing experts from the host arrays over PCIe into
+ * their slots, so the host arrays must be pinned (hipHostMalloc, or torch's
+ * pin_memory) and stay alive as long as the cache.  Ordering: a residency
+ * step runs on the copy stream after the work enqueued so far on the compute
+ * stream (which may still read the slots it refills) and after this cache's
+ * earlier steps; the compute stream's later work waits for it.  Nothing waits
+ * for the host.  bf16 layers only.  A cache
  * holds the experts either in bf16 (moe_cache_create) or as MXFP4 codes and
  * scales (moe_cache_create_mxfp4: [P3] §5.2 serves with the expert cache and
  * 4-bit experts together; a slot then costs about a quarter of the HBM and of
@@ -405,10 +409,11 @@ typedef struct {
  * (0 on invalid dims or slots < 1). */
 size_t moe_cache_pool_bytes(const moe_dims_t* dims, int32_t slots);
 
-/* host_w1/host_w3 [E,I,H], host_w2 [E,H,I] (host memory, dims->dtype, owned by
- * the caller and kept alive as long as the cache); pool: device memory of at
- * least moe_cache_pool_bytes.  Only H, E, I and dtype of dims matter here.
- * On success *cache receives the new object. */
+/* host_w1/host_w3 [E,I,H], host_w2 [E,H,I] (pinned host memory, dims->dtype,
+ * owned by the caller and kept alive as long as the cache; not pinned:
+ * MOE_ERR_INVALID_ARG); pool: device memory of at least moe_cache_pool_bytes
+ * (slots <= 1024).  Only H, E, I and dtype of dims matter here.  On success
+ * *cache receives the new object. */
 moe_status_t moe_cache_create(const moe_dims_t* dims, int32_t slots, const void* host_w1,
                               const void* host_w3, const void* host_w2, void* pool,
                               size_t pool_bytes, moe_expert_cache_t** cache);
@@ -433,26 +438,35 @@ moe_status_t moe_cache_create_mxfp4(const moe_dims_t* dims, int32_t slots,
 void moe_cache_destroy(moe_expert_cache_t* cache);
 
 /* Make the n experts in `experts` (host array, ids in [0, E), duplicates
- * allowed) resident: enqueue their copies on copy_stream, the table update
- * on stream, and make stream wait for the copies.  More distinct experts than
- * slots: MOE_ERR_UNSUPPORTED, nothing changes.  info (host) may be NULL. */
+ * allowed) resident: enqueue the residency step and the copies on
+ * copy_stream, and make stream wait for them (a prefetch ahead of the batch
+ * that needs them).  More distinct experts than slots: MOE_ERR_UNSUPPORTED,
+ * nothing enqueued.  info (host) may be NULL; if given, the call waits for
+ * the step and reports it. */
 moe_status_t moe_cache_load(moe_expert_cache_t* cache, const int32_t* experts, int32_t n,
                             void* copy_stream, void* stream, moe_cache_step_t* info);
 
-/* Host copy of the expert -> slot table (-1: not resident), slot_of [E]. */
+/* Host copy of the expert -> slot table (-1: not resident), slot_of [E];
+ * waits for the cache's last residency step. */
 moe_status_t moe_cache_slots(const moe_expert_cache_t* cache, int32_t* slot_of);
 
+/* The cache's last residency step (moe_cache_load or a cached layer): waits
+ * for it and fills info; MOE_ERR_UNSUPPORTED if that batch needed more
+ * distinct experts than slots (the cache was left unchanged). */
+moe_status_t moe_cache_last_step(const moe_expert_cache_t* cache, moe_cache_step_t* info);
+
 /* moe_layer_forward with the routed experts' weights in an expert cache: after
- * the gate, route and permute, the per-expert row counts come back to the host
- * (this call waits for `stream` there), the experts with rows are made
- * resident (moe_cache_load on copy_stream), and the grouped GEMMs read each
+ * the gate, route and permute, the experts with kept rows are made resident
+ * by a residency step on copy_stream (decided on the device from the
+ * per-expert row counts; no host round trip), and the grouped GEMMs read each
  * expert's weights from its slot.  The shared expert (dims->I_shared > 0) is
  * given as in moe_layer_forward and is not cached.  The output is bit for bit
- * that of moe_layer_forward with the same weights.  info (host) may be NULL.
- * The two exceptions to the conventions above: the host waits for `stream`
- * mid-call, and a batch that needs more distinct experts than the cache has
- * slots fails with MOE_ERR_UNSUPPORTED after the routing steps were enqueued
- * (slots >= min(E, T*k) rules that out). */
+ * that of moe_layer_forward with the same weights.  info (host) may be NULL;
+ * if given, the call waits for the layer's residency step at its end and
+ * reports it.  A batch that needs more distinct experts than the cache has
+ * slots leaves the cache unchanged and the output unspecified, reported as
+ * MOE_ERR_UNSUPPORTED by this call (with info) or by moe_cache_last_step
+ * (slots >= min(E, T*k) rules it out). */
 moe_status_t moe_layer_forward_cached(const moe_dims_t* dims, const void* x, const void* wg,
                                       const float* bias, moe_expert_cache_t* cache,
                                       const void* ws1, const void* ws3, const void* ws2, void* y,

@@ -19,7 +19,8 @@ EXPORTS = ("moe_status_str", "moe_capacity", "moe_workspace_bytes", "moe_gate", 
            "moe_cache_load", "moe_cache_slots", "moe_layer_forward", "moe_layer_forward_fp8",
            "moe_layer_forward_cached", "moe_static_scratch_bytes", "moe_layer_forward_static",
            "moe_quantize_mxfp8", "moe_expert_ffn_w4a8", "moe_layer_forward_w4a8",
-           "moe_cache_pool_bytes_mxfp4", "moe_cache_create_mxfp4", "moe_layer_forward_cached_w4a8")
+           "moe_cache_pool_bytes_mxfp4", "moe_cache_create_mxfp4", "moe_layer_forward_cached_w4a8",
+           "moe_cache_last_step")
 MOE_BIAS_SOFTMAX, MOE_BIAS_SELECT = 0, 1
 
 
@@ -120,6 +121,8 @@ def lib():
         L.moe_cache_destroy.argtypes = [p]
         L.moe_cache_load.restype = i32
         L.moe_cache_load.argtypes = [p, p, i32, p, p, C.POINTER(MoeCacheStep)]
+        L.moe_cache_last_step.restype = i32
+        L.moe_cache_last_step.argtypes = [p, C.POINTER(MoeCacheStep)]
         L.moe_cache_slots.restype = i32
         L.moe_cache_slots.argtypes = [p, p]
         L.moe_layer_forward_cached.restype = i32

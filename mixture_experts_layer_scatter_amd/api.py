@@ -357,13 +357,21 @@ class ExpertCache:
                                       C.byref(h)), "moe_cache_create")
         self.handle = h
 
-    def load(self, experts, copy_stream=None, stream=None) -> dict:
+    def load(self, experts, copy_stream=None, stream=None, wait=True):
+        """Make `experts` resident (a prefetch).  wait: also wait for the step and return its
+        report (else return None at once)."""
         import numpy as np
         ids = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
         info = MoeCacheStep()
         _check(_lib.lib().moe_cache_load(self.handle, ids.ctypes.data if ids.size else None,
                                          int(ids.size), _stream(copy_stream), _stream(stream),
-                                         C.byref(info)), "moe_cache_load")
+                                         C.byref(info) if wait else None), "moe_cache_load")
+        return _step_dict(info) if wait else None
+
+    def last_step(self) -> dict:
+        """The report of the cache's last residency step (waits for it)."""
+        info = MoeCacheStep()
+        _check(_lib.lib().moe_cache_last_step(self.handle, C.byref(info)), "moe_cache_last_step")
         return _step_dict(info)
 
     def slots(self):
@@ -382,9 +390,10 @@ class ExpertCache:
 
 
 def layer_forward_cached(d: Dims, x, wg, bias, cache: ExpertCache, shared=None, y=None, ws=None,
-                         debug=None, stream=None, copy_stream=None):
-    """The fused layer with the routed experts' weights in an ExpertCache; returns (y, step info).
-    Waits for `stream` once, after the routing, to learn which experts are needed."""
+                         debug=None, stream=None, copy_stream=None, wait=True):
+    """The fused layer with the routed experts' weights in an ExpertCache; returns (y, step
+    info).  wait: wait for the layer's residency step at the end and report it (else the call
+    only enqueues and the info is None; ExpertCache.last_step reports it later)."""
     dt = d.torch_dtype
     if y is None:
         y = torch.empty((d.T, d.H), dtype=dt, device=x.device)
@@ -401,12 +410,12 @@ def layer_forward_cached(d: Dims, x, wg, bias, cache: ExpertCache, shared=None, 
         cache.handle, _ptr(s1, dt, "ws1"), _ptr(s3, dt, "ws3"), _ptr(s2, dt, "ws2"), _ptr(y, dt, "y"),
         C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream), _stream(copy_stream if copy_stream is not None else stream),
-        C.byref(info)), "moe_layer_forward_cached")
-    return y, _step_dict(info)
+        C.byref(info) if wait else None), "moe_layer_forward_cached")
+    return y, (_step_dict(info) if wait else None)
 
 
 def layer_forward_cached_w4a8(d: Dims, x, wg, bias, cache: ExpertCache, shared=None, y=None,
-                              ws=None, debug=None, stream=None, copy_stream=None):
+                              ws=None, debug=None, stream=None, copy_stream=None, wait=True):
     """The fused layer on MXFP8 activations with the routed experts' MXFP4 weights in an MXFP4
     ExpertCache; shared: the shared expert's (codes, scales) pairs on the device, or None.
     Returns (y, step info)."""
@@ -427,8 +436,8 @@ def layer_forward_cached_w4a8(d: Dims, x, wg, bias, cache: ExpertCache, shared=N
         _ptr(t3, u8, "ws3s"), _ptr(e2, u8, "ws2q"), _ptr(t2, u8, "ws2s"), _ptr(y, dt, "y"),
         C.byref(dbg) if dbg is not None else None, _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream), _stream(copy_stream if copy_stream is not None else stream),
-        C.byref(info)), "moe_layer_forward_cached_w4a8")
-    return y, _step_dict(info)
+        C.byref(info) if wait else None), "moe_layer_forward_cached_w4a8")
+    return y, (_step_dict(info) if wait else None)
 
 
 def layer_forward(d: Dims, x, wg, bias, w1, w3, w2, shared=None, y=None, ws=None, debug=None,

@@ -639,17 +639,10 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
   a.row_token = row_token;
   MOE_TRY(launch_permute(a, s));
   if (cu) {
-    // the experts with kept rows must be resident: their counts come back to the host, the
-    // missing ones are copied in on the copy stream and the compute stream waits for them
-    std::vector<int32_t> counts(E), need;
-    MOE_TRY(hipMemcpyAsync(counts.data(), at<int32_t>(ws, L.counts), (size_t)E * 4,
-                           hipMemcpyDeviceToHost, s));
-    MOE_TRY(hipStreamSynchronize(s));
-    for (int e = 0; e < E; ++e)
-      if (counts[e] > 0) need.push_back(e);
-    const moe_status_t ls = moe_cache_load(cu->cache, need.data(), (int32_t)need.size(),
-                                           cu->copy_stream, s, cu->info);
-    if (ls != MOE_OK) return ls;
+    // the experts with kept rows must be resident: the cache decides on the device from the
+    // per-expert counts and copies the missing experts in on the copy stream, and this stream
+    // waits for them (no host round trip)
+    MOE_TRY(cache_enqueue_counts(cu->cache, at<int32_t>(ws, L.counts), cu->copy_stream, s));
   }
   // 4-5. grouped gate-up (rows gathered straight from x) and down
   const int G = E + (fold ? 1 : 0);
@@ -705,6 +698,8 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
       MOE_TRY(hipMemcpyAsync(dbg->n_dropped, at<int32_t>(ws, L.n_dropped), 4,
                              hipMemcpyDeviceToDevice, s));
   }
+  // the cache's residency step, when the caller asked for it: waits for the step itself
+  if (cu && cu->info) return moe_cache_last_step(cu->cache, cu->info);
   return MOE_OK;
 }
 

@@ -187,6 +187,11 @@ struct CacheView {
 struct moe_expert_cache;
 namespace moe {
 CacheView cache_view(const moe_expert_cache* c);
+// the cached layer's residency step: the experts with rows in counts[E] (device) made resident,
+// decided and copied on the device on copy stream cs after the work so far on ks, which then
+// waits for them
+hipError_t cache_enqueue_counts(moe_expert_cache* c, const int32_t* counts, hipStream_t cs,
+                                hipStream_t ks);
 
 // quant.hip: per-row FP8 E4M3 quantisation of a [rows, K] bf16 or fp32 matrix (K % 8 == 0)
 hipError_t launch_quantize_fp8(const void* w, int bf16, int64_t rows, int K, uint8_t* q,

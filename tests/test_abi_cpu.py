@@ -201,6 +201,8 @@ def test_cache_argument_checks():
     assert lib.moe_cache_create(C.byref(_dims(dtype=L.MOE_F32)), 4, p, p, p, p, n,
                                 C.byref(out)) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_cache_load(None, None, 0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_last_step(None, C.byref(L.MoeCacheStep())) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_pool_bytes(C.byref(d), 1025) == 0  # one planning thread per slot
     assert lib.moe_cache_slots(None, p) == L.MOE_ERR_INVALID_ARG
     lib.moe_cache_destroy(None)  # no-op
     assert lib.moe_layer_forward_cached(C.byref(d), p, p, None, None, None, None, None, p, None,

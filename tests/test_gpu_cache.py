@@ -7,6 +7,10 @@
   read the same weight values from other addresses), over a sequence of batches whose routing
   changes, with evictions; and one cached call, with experts in slots other than their ids,
   against the oracle directly.
+* Residency is decided on the device: the layer without a report only enqueues, and its step
+  read afterwards still follows the LRU model; a batch needing more experts than slots leaves
+  the cache unchanged and is reported; pageable host arrays are refused.
+* The same for an MXFP4 cache feeding the layer on MXFP8 activations.
 """
 import numpy as np
 import pytest
@@ -273,3 +277,80 @@ def test_cached_w4a8_layer_against_oracle():
     assert any(s >= 0 and s != e for e, s in enumerate(slot_of))
     check_against_oracle(w, g, Mxfp4Weights(w, cache=False), None, tag=" (cached w4a8)",
                          ffn=oracle.expert_ffn_a8)
+
+
+# ---- device-side residency: no host wait in the layer ---------------------------------------
+
+def test_cached_layer_enqueue_only():
+    """With no report asked for, the cached layer only enqueues: its residency step is decided on
+    the device.  Each batch's output still equals the uncached layer's bit for bit, and the
+    cache's last step (read afterwards) equals the LRU model's."""
+    need_gpu()
+    rng = np.random.default_rng(5)
+    E, slots, T, k, H, I = 24, 8, 4, 2, 256, 128
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    wg = bf16_normal(rng, (E, H), 1 / np.sqrt(H))
+    d = moe.Dims(T=T, H=H, E=E, k=k, I=I)
+    cache = moe.ExpertCache(d, slots, _pinned(W1), _pinned(W3), _pinned(W2))
+    dw1, dw3, dw2, dwg = dev(W1), dev(W3), dev(W2), dev(wg)
+    ref = LRUCache(E, slots)
+    ws = moe.workspace(d)
+    for step in range(10):
+        x = dev(bf16_normal(rng, (T, H)))
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        y, info = moe.layer_forward_cached(d, x, dwg, None, cache, None, ws=ws,
+                                           debug=dict(counts=counts), wait=False)
+        assert info is None
+        y_ref = moe.layer_forward(d, x, dwg, None, dw1, dw3, dw2, None)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), bits(y_ref)), step
+        last = cache.last_step()
+        hits, loads, ev = ref.request(np.nonzero(counts.cpu().numpy())[0].tolist())
+        assert (last["hits"], last["loads"], last["evictions"]) == (len(hits), len(loads), len(ev))
+        assert cache.slots().tolist() == ref.slot_of, step
+    cache.close()
+
+
+def test_cached_layer_more_experts_than_slots():
+    """A batch that needs more distinct experts than the cache has slots leaves the cache
+    unchanged and is reported (MOE_ERR_UNSUPPORTED) by the call and by last_step; the next batch
+    that fits runs normally."""
+    need_gpu()
+    rng = np.random.default_rng(6)
+    E, slots, H, I = 16, 3, 256, 128
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    wg = bf16_normal(rng, (E, H), 1 / np.sqrt(H))
+    cache = moe.ExpertCache(moe.Dims(T=1, H=H, E=E, k=1, I=I), slots, _pinned(W1), _pinned(W3),
+                            _pinned(W2))
+    dw1, dw3, dw2, dwg = dev(W1), dev(W3), dev(W2), dev(wg)
+    cache.load([1, 2])
+    before = cache.slots().tolist()
+    d = moe.Dims(T=32, H=H, E=E, k=2, I=I)  # 64 picks over 16 experts: more than 3 distinct
+    x = dev(bf16_normal(rng, (32, H)))
+    with pytest.raises(moe.MoeError) as err:
+        moe.layer_forward_cached(d, x, dwg, None, cache, None)
+    assert err.value.status == 2  # MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError):
+        cache.last_step()
+    assert cache.slots().tolist() == before
+    # one token, top-1: one expert, which fits
+    d1 = moe.Dims(T=1, H=H, E=E, k=1, I=I)
+    x1 = dev(bf16_normal(rng, (1, H)))
+    y, info = moe.layer_forward_cached(d1, x1, dwg, None, cache, None)
+    y_ref = moe.layer_forward(d1, x1, dwg, None, dw1, dw3, dw2, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), bits(y_ref))
+    assert info["requested"] == 1
+    cache.close()
+
+
+def test_cache_needs_pinned_host_memory():
+    """The copy kernel reads the host arrays over PCIe, so pageable ones are refused."""
+    need_gpu()
+    rng = np.random.default_rng(7)
+    E, H, I = 4, 64, 64
+    W1, W3, W2 = _host_weights(rng, E, H, I)
+    pageable = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) for a in (W1, W3, W2)]
+    with pytest.raises(moe.MoeError) as err:
+        moe.ExpertCache(moe.Dims(T=1, H=H, E=E, k=1, I=I), 2, *pageable)
+    assert err.value.status == 1  # MOE_ERR_INVALID_ARG
