@@ -47,6 +47,12 @@ def main():
                          "of this many slots, filled from pinned host memory (cold and warm)")
     ap.add_argument("--bias-mode", choices=("softmax", "select"), default="softmax",
                     help="how a workload's routing bias enters: inside the softmax, or ranking only")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload with this many tokens instead of its own (e.g. a "
+                         "small decode batch)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one layer into a HIP graph and time its replays "
+                         "(layer.graph_ms_per_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sub-workloads",
                     default="qwen3_prefill,dsv3_decode,skewed_capacity,dsv3_decode:w4a8,"
@@ -80,6 +86,8 @@ def main():
     torch.cuda.set_device(dev)
     default_run = args.workload is None
     w = moe_synth.get(args.workload or "mixtral_prefill")
+    if args.tokens > 0:
+        w = w.scaled(args.tokens)
     r = measure(w, args, args.steps, args.warmup, cache_slots=args.cache_slots)
     out = {
         "metric": METRIC,
@@ -238,6 +246,21 @@ def measure(w, args, steps, warmup, cache_slots=0, weights=None):
     layer_ms = [c.elapsed_ms(e) for c, e in spans]
     ms_per_step = wall * 1e3 / steps
 
+    # the same layer as one HIP graph (every step only enqueues: no host wait, no allocation),
+    # replayed `steps` times: what a launch-bound decode loop gets
+    graph_ms = None
+    if getattr(args, "graph", False):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+
     # per-stage breakdown (untimed extra steps)
     stage = [Event() for _ in range(_lib.NUM_EVENTS)]
     stage_ms = np.zeros(_lib.NUM_EVENTS - 1)
@@ -343,6 +366,9 @@ def measure(w, args, steps, warmup, cache_slots=0, weights=None):
              "min_topk_margin": None if min_margin is None else float(f"{min_margin:.3g}"),
              "load_stats": load,
              **({"lowbit_vs_bf16_weights_rel_l2": round(quant_err, 5)} if lowbit else {}),
+             **({"graph_ms_per_step": round(graph_ms, 4),
+                 "graph_tokens_per_s": round(w.T / (graph_ms * 1e-3), 1)}
+                if graph_ms is not None else {}),
              **({"expert_cache": cache_res} if cache_res is not None else {})}
     del t, ws, y
     return {"tokens_per_s": round(w.T / layer_s, 1), "ms_per_step": round(ms_per_step, 4),
