@@ -181,3 +181,38 @@ def test_layer_w4a8_shared_expert_of_another_width():
     need_gpu()
     w = moe_synth.Workload("w4a8_shared_other", 203, T=100, H=256, E=16, k=4, I=128, I_shared=256)
     check_layer_w4a8(w)
+
+
+def _random_workloads(n=8, seed=4242):
+    """Seeded small layer shapes for the 4-bit paths (bf16, H and I in 128s): E from 1 to 130,
+    every k, a shared expert of the routed width or another width, capacity factors that drop
+    slots, the Zipf bias in both modes, raw softmax weights, token counts from 1 up."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        H = int(rng.choice([128, 256, 512]))
+        E = int(rng.choice([1, 3, 16, 64, 130]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        I = int(rng.choice([128, 256]))
+        shared = int(rng.choice([0, I, 384]))
+        cf = [None, 0.5, 1.0, 1.25][int(rng.integers(0, 4))]
+        zipf = 1.2 if rng.random() < 0.4 else None
+        T = int(rng.choice([1, 7, 100, 333, 1000]))
+        out.append(moe_synth.Workload(f"random4b{i}", 300 + i, T=T, H=H, E=E, k=k, I=I,
+                                      I_shared=shared, capacity_factor=cf, zipf_s=zipf,
+                                      renormalize=int(rng.random() < 0.8),
+                                      bias_mode=i % 2 if zipf else 0))
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "w4a8"])
+@pytest.mark.parametrize("w", _random_workloads(), ids=lambda w: (
+    f"{w.name}-T{w.T}-H{w.H}-E{w.E}-k{w.k}-I{w.I}-Is{w.I_shared}-cf{w.capacity_factor}"
+    f"-z{w.zipf_s}-r{w.renormalize}-b{w.bias_mode}"))
+def test_random_shapes_4bit_every_token(w, fmt):
+    need_gpu()
+    if fmt == "w4a8":
+        check_layer_w4a8(w)
+    else:
+        from test_gpu_mxfp4 import check_layer_mxfp4
+        check_layer_mxfp4(w)
