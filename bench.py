@@ -228,23 +228,30 @@ def measure(w, args, steps, warmup, cache_slots=0, weights=None):
         step()
     torch.cuda.synchronize()
 
-    # timed region: events around the dominant kernel and around the whole layer, on the launch
-    # stream (the layer's per-step spans give the median and the minimum next to the mean)
+    # timed region: events around the dominant kernel, on the launch stream (the roofline's
+    # launch time); nothing else is recorded in it
     dom = (_lib.EV_PERMUTE, _lib.EV_GATE_UP)
     pairs = [(Event(), Event()) for _ in range(steps)]
-    spans = [(Event(), Event()) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for (a, b), (c, e) in zip(pairs, spans):
+    for a, b in pairs:
         ev = [None] * _lib.NUM_EVENTS
         ev[dom[0]], ev[dom[1]] = a.handle.value, b.handle.value
-        ev[_lib.EV_START], ev[_lib.EV_END] = c.handle.value, e.handle.value
         step(dict(events=ev))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gu_ms = [a.elapsed_ms(b) for a, b in pairs]
-    layer_ms = [c.elapsed_ms(e) for c, e in spans]
     ms_per_step = wall * 1e3 / steps
+
+    # the layer's per-step spans (events at its start and end), for the median and the minimum
+    # next to the mean: as many steps again, outside the timed region
+    spans = [(Event(), Event()) for _ in range(steps)]
+    for c, e in spans:
+        ev = [None] * _lib.NUM_EVENTS
+        ev[_lib.EV_START], ev[_lib.EV_END] = c.handle.value, e.handle.value
+        step(dict(events=ev))
+    torch.cuda.synchronize()
+    layer_ms = [c.elapsed_ms(e) for c, e in spans]
 
     # the same layer as one HIP graph (every step only enqueues: no host wait, no allocation),
     # replayed `steps` times: what a launch-bound decode loop gets
