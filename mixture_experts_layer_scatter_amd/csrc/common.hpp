@@ -99,9 +99,12 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_pack_rows(const void* x, const int32_t* row_token, const int32_t* n_rows,
                             int max_rows, int H, int elem_bytes, void* xp, hipStream_t s);
 
-// tile map of the grouped GEMMs: tile_start[g] = sum over g' < g of ceil(rows_g' / bm) * nt
+// tile map of the grouped GEMMs: tile_start[g] = sum over g' < g of ceil(rows_g' / bm) * nt,
+// and (info non-null) one entry per tile t: {g, tile_start[g], offsets[g], rows of g}, so that a
+// GEMM finds a tile's group with one load instead of a search over the groups
 hipError_t launch_tile_map(const int32_t* offsets, int G, int bm0, int nt0, int32_t* start0,
-                           int bm1, int nt1, int32_t* start1, hipStream_t s);
+                           int4* info0, int bm1, int nt1, int32_t* start1, int4* info1,
+                           hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const void* yp, const int32_t* pos, const float* w, const void* ys,
@@ -155,6 +158,7 @@ struct GroupedGemm {
   int G_routed;
   int static_rows;           // rows of the single group when offsets == null
   const int32_t* tile_start; // [G+1] device tile map, or null with offsets == null
+  const int4* tile_info;     // [tiles] per-tile entries of that map (launch_tile_map), or null
   int ksplit;                // > 1: split the reduction (fp32 output only), partial s at
   int64_t c_split_stride;    //      c + s * c_split_stride (elements)
   // Split of the last, partly filled round of tiles (each XCD's chunk): when set, a tile of

@@ -306,7 +306,16 @@ template <class SH, int GN>
 __device__ __forceinline__ TileLoc locate_tile(const GroupedGemm& p, int tile) {
   int g = 0, row_base = 0, rows = p.static_rows, li = tile;
   tile = __builtin_amdgcn_readfirstlane(tile);
-  if (p.tile_start) {
+  if (p.tile_info) {
+    // the tile map's own entry for this tile: one 16-byte scalar load (the search below costs a
+    // dependent load per halving of the groups)
+    typedef const __attribute__((address_space(4))) i32x4* cptr4;
+    const i32x4 e = ((cptr4)p.tile_info)[tile];
+    g = e[0];
+    li = tile - e[1];
+    row_base = e[2];
+    rows = e[3];
+  } else if (p.tile_start) {
     int lo = 0, hi2 = p.G;  // largest g with tile_start[g] <= tile
     while (hi2 - lo > 1) {
       const int mid = (lo + hi2) >> 1;

@@ -228,13 +228,16 @@ hipError_t launch_pack_rows(const void* x, const int32_t* row_token, const int32
 // ---- tile map of the grouped GEMMs ----------------------------------------------------------
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
                                                         int G, int bm0, int nt0,
-                                                        int32_t* __restrict__ start0, int bm1,
-                                                        int nt1, int32_t* __restrict__ start1) {
+                                                        int32_t* __restrict__ start0,
+                                                        int4* __restrict__ info0, int bm1,
+                                                        int nt1, int32_t* __restrict__ start1,
+                                                        int4* __restrict__ info1) {
   __shared__ int32_t buf[2 * 1024];
   __shared__ int32_t tmp[1024 / kWave + 1];
   for (int pass = 0; pass < 2; ++pass) {
     const int bm = pass ? bm1 : bm0, nt = pass ? nt1 : nt0;
     int32_t* out = pass ? start1 : start0;
+    int4* info = pass ? info1 : info0;
     if (!out) continue;
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
       const int rows = offsets[g + 1] - offsets[g];
@@ -244,13 +247,28 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     const int total = block_exclusive_scan2<1024>(buf, tmp, G);
     for (int g = threadIdx.x; g < G; g += blockDim.x) out[g] = buf[g];
     if (threadIdx.x == 0) out[G] = total;
+    if (info) {
+      __syncthreads();
+      // tile t belongs to the largest g with tile_start[g] <= t (groups without tiles share
+      // their start with the next group, and never hold the largest such g for a t below it)
+      for (int t = threadIdx.x; t < total; t += blockDim.x) {
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (buf[mid] <= t) lo = mid;
+          else hi = mid;
+        }
+        info[t] = make_int4(lo, buf[lo], offsets[lo], offsets[lo + 1] - offsets[lo]);
+      }
+    }
     __syncthreads();
   }
 }
 
 hipError_t launch_tile_map(const int32_t* offsets, int G, int bm0, int nt0, int32_t* start0,
-                           int bm1, int nt1, int32_t* start1, hipStream_t s) {
-  tile_map_kernel<<<1, 1024, 0, s>>>(offsets, G, bm0, nt0, start0, bm1, nt1, start1);
+                           int4* info0, int bm1, int nt1, int32_t* start1, int4* info1,
+                           hipStream_t s) {
+  tile_map_kernel<<<1, 1024, 0, s>>>(offsets, G, bm0, nt0, start0, info0, bm1, nt1, start1, info1);
   return hipGetLastError();
 }
 
