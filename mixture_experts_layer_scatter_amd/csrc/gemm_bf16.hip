@@ -42,9 +42,10 @@
 //    so the tiles of a group cost about the same, which keeps the workgroups of
 //    an XCD in step over the operand panels they share.
 //  * Groups (experts) have ragged row counts known only on the device.  A
-//    device tile map (tile_start) lists every group's tiles; a persistent grid
-//    walks it.  Tiles are dealt out XCD by XCD (workgroups go round-robin over
-//    the 8 XCDs), so the workgroups sharing one XCD's L2 take consecutive tiles;
+//    device tile map (tile_start, with one entry per tile naming its group)
+//    lists every group's tiles; a persistent grid walks it.  Tiles are dealt
+//    out XCD by XCD (workgroups go round-robin over the 8 XCDs), so the
+//    workgroups sharing one XCD's L2 take consecutive tiles;
 //    inside a group, tiles run column-group by column-group (GN column tiles x
 //    all row tiles), so concurrent tiles reuse the same weight and row panels.
 //  * Gate-up: the B tile interleaves 32-row blocks of W1 and W3, so each
