@@ -125,10 +125,11 @@ def test_expert_ffn_f32(counts, H, I):
 
 
 @pytest.mark.parametrize("dtype,shared", [("bf16", False), ("bf16", True), ("f32", True)])
-def test_combine(dtype, shared):
+@pytest.mark.parametrize("k", [4, 11])  # 11: two blocks of slots read together
+def test_combine(dtype, shared, k):
     need_gpu()
-    rng = np.random.default_rng(11)
-    T, H, k = 333, 256, 4
+    rng = np.random.default_rng(11 + k)
+    T, H = 333, 256
     R = T * k - 100
     if dtype == "bf16":
         yp = bf16_normal(rng, (T * k, H))
@@ -139,7 +140,7 @@ def test_combine(dtype, shared):
     pos = rng.permutation(T * k).astype(np.int32).reshape(T, k)
     pos[pos >= R] = -1
     w = rng.random((T, k), dtype=np.float32)
-    d = moe.Dims(T=T, H=H, E=8, k=k, I=64, dtype=dtype)
+    d = moe.Dims(T=T, H=H, E=16, k=k, I=64, dtype=dtype)
     y = torch.empty((T, H), dtype=d.torch_dtype, device="cuda")
     moe.combine(d, dev(yp), dev(pos), dev(w), None if ys is None else dev(ys), y)
     got = f64(y)
