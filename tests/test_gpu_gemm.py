@@ -125,7 +125,7 @@ def test_expert_ffn_f32(counts, H, I):
 
 
 @pytest.mark.parametrize("dtype,shared", [("bf16", False), ("bf16", True), ("f32", True)])
-@pytest.mark.parametrize("k", [4, 11])  # 11: two blocks of slots read together
+@pytest.mark.parametrize("k", [4, 11])
 def test_combine(dtype, shared, k):
     need_gpu()
     rng = np.random.default_rng(11 + k)
