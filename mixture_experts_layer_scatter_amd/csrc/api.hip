@@ -21,7 +21,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Byte layout of the workspace; one layout serves every call.
 struct Layout {
   size_t tail, gate_part, logits, ids, w, tile_hist, tile_base, raw, counts, offsets, n_dropped, ts_gu, ts_dn,
-      ti_gu, ti_dn, pos,
+      ti_gu, ti_dn, ti_cap, pos,
       dropped, row_token, xq, act, yp, yps, total;
 };
 
@@ -88,8 +88,9 @@ Layout layout(const moe_dims_t* d) {
   {
     const size_t cols = imax > (size_t)d->H ? imax : (size_t)d->H;
     const size_t tiles = ((rows + 31) / 32 + E + 2) * ((cols + 127) / 128);
-    L.ti_gu = take(d->dtype == MOE_BF16 ? tiles * 16 : 0);
-    L.ti_dn = take(d->dtype == MOE_BF16 ? tiles * 16 : 0);
+    L.ti_cap = d->dtype == MOE_BF16 ? tiles : 0;
+    L.ti_gu = take(L.ti_cap * 16);
+    L.ti_dn = take(L.ti_cap * 16);
   }
   L.pos = take(n * 4);
   L.dropped = take(n);
@@ -258,7 +259,8 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const uint8_t* a_m
                    const int32_t* row_map,
                    int64_t a_rows, int64_t max_rows, const int32_t* offsets, int G, int G_routed,
                    const ExpertWeights& W, const ExpertWeights* X, void* act, void* out,
-                   int32_t* ts_gu, int32_t* ts_dn, int4* ti_gu, int4* ti_dn, int avg_rows,
+                   int32_t* ts_gu, int32_t* ts_dn, int4* ti_gu, int4* ti_dn, size_t ti_cap,
+                   int avg_rows,
                    float* tail, hipStream_t s,
                    void* const* ev = nullptr, const int32_t* group_slot = nullptr) {
   const bool bf16 = d->dtype == MOE_BF16;
@@ -280,6 +282,12 @@ hipError_t run_ffn(const moe_dims_t* d, int I, const void* a, const uint8_t* a_m
     gemm_f32_tiling(d->H, &bm_dn, &nt_dn);
   }
   if (!bf16) ti_gu = ti_dn = nullptr;  // the fp32 GEMMs search the map
+  // per-tile entries only where the launch's tile count fits the table (else the GEMM searches)
+  auto fits = [&](int bm, int nt) {
+    return (size_t)((max_rows + bm - 1) / bm + G) * (size_t)nt <= ti_cap;
+  };
+  if (ti_gu && !fits(bm_gu, nt_gu)) ti_gu = nullptr;
+  if (ti_dn && !fits(bm_dn, nt_dn)) ti_dn = nullptr;
   hipError_t e = launch_tile_map(offsets, G, bm_gu, nt_gu, ts_gu, ti_gu, bm_dn, nt_dn, ts_dn, ti_dn, s);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, MOE_EV_PERMUTE, s)) != hipSuccess) return e;
@@ -496,7 +504,7 @@ moe_status_t expert_ffn_impl(const moe_dims_t* d, const void* x_packed, const in
   }
   MOE_TRY(run_ffn(d, d->I, a, a_mx, nullptr, n, n, offsets, d->E, d->E, W, nullptr,
                   at<void>(ws, L.act), y_packed, at<int32_t>(ws, L.ts_gu),
-                  at<int32_t>(ws, L.ts_dn), at<int4>(ws, L.ti_gu), at<int4>(ws, L.ti_dn), avg, at<float>(ws, L.tail), s));
+                  at<int32_t>(ws, L.ts_dn), at<int4>(ws, L.ti_gu), at<int4>(ws, L.ti_dn), L.ti_cap, avg, at<float>(ws, L.tail), s));
   return MOE_OK;
 }
 
@@ -673,7 +681,7 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
   }
   MOE_TRY(run_ffn(d, d->I, xa, xa_mx, row_token, T, max_rows, offsets, G, E, W, fold ? &SW : nullptr,
                   at<void>(ws, L.act), yp, at<int32_t>(ws, L.ts_gu), at<int32_t>(ws, L.ts_dn),
-                  at<int4>(ws, L.ti_gu), at<int4>(ws, L.ti_dn), avg,
+                  at<int4>(ws, L.ti_gu), at<int4>(ws, L.ti_dn), L.ti_cap, avg,
                   at<float>(ws, L.tail), s, ev, group_slot));
   const void* ys = nullptr;
   const int32_t* ys_row0 = nullptr;
@@ -689,7 +697,7 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
     MOE_TRY(hipGetLastError());
     MOE_TRY(run_ffn(d, d->I_shared, xa, xa_mx, nullptr, T, T, off2, 1, 1, SW, nullptr,
                     at<void>(ws, L.act), at<void>(ws, L.yps), at<int32_t>(ws, L.ts_gu),
-                    at<int32_t>(ws, L.ts_dn), at<int4>(ws, L.ti_gu), at<int4>(ws, L.ti_dn), T, at<float>(ws, L.tail), s));
+                    at<int32_t>(ws, L.ts_dn), at<int4>(ws, L.ti_gu), at<int4>(ws, L.ti_dn), L.ti_cap, T, at<float>(ws, L.tail), s));
     ys = at<void>(ws, L.yps);
   }
   // 6. weighted combine back into token order
