@@ -43,7 +43,11 @@
  *    valid no-op.
  *  - Deterministic: identical inputs give bitwise-identical outputs (no
  *    floating-point atomics; every sum has a fixed order).
- *  - Thread-safe: the library holds no mutable global state.
+ *  - Thread-safe: calls from several threads may run at once.  The library's
+ *    global state is set once per device and process (each kernel's LDS size
+ *    attribute, the compute-unit count), written with atomics; the exceptions
+ *    are an expert cache handle (one thread at a time) and the scratch array
+ *    of moe_layer_forward_static (overlapping calls on one device race).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
