@@ -15,9 +15,11 @@
  *
  * Conventions shared by every call:
  *  - Every array pointer is a DEVICE pointer; the caller allocates and owns it.
- *    The library never allocates, frees or retains a pointer after a call
- *    returns.  Scratch memory comes from the caller's workspace (`ws`,
- *    `ws_bytes`), sized by moe_workspace_bytes().
+ *    The library never allocates device memory, and retains no pointer after a
+ *    call returns, except the expert cache handle: moe_cache_create allocates
+ *    its host bookkeeping and keeps the caller's pool and pinned host weights
+ *    until moe_cache_destroy.  Scratch memory comes from the caller's
+ *    workspace (`ws`, `ws_bytes`), sized by moe_workspace_bytes().
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work and return; outputs are ready when the stream reaches that point.
  *    No call synchronises with the host, except the expert cache's reports:
