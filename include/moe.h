@@ -17,8 +17,8 @@
  *  - Every array pointer is a DEVICE pointer; the caller allocates and owns it.
  *    The library never allocates device memory, and retains no pointer after a
  *    call returns, except the expert cache handle: moe_cache_create allocates
- *    its host bookkeeping and keeps the caller's pool and pinned host weights
- *    until moe_cache_destroy.  Scratch memory comes from the caller's
+ *    its host bookkeeping and two HIP events, and keeps the caller's pool and
+ *    pinned host weights, until moe_cache_destroy.  Scratch memory comes from the caller's
  *    workspace (`ws`, `ws_bytes`), sized by moe_workspace_bytes().
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work and return; outputs are ready when the stream reaches that point.
