@@ -677,9 +677,16 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     }
   };
   // local k-step lk of the current tile into LDS slots `slot` (token rows) and `bslot` (weights);
-  // lk >= ktn loads nothing
+  // lk >= ktn loads nothing.  The 256 x 256 MXFP8 tiles instead re-read the tile's last k-step
+  // there (into a slot nothing reads before the next tile's loads): with the masked form the
+  // compiler turned the offset selects into branches inside their k-loop, splitting the region
+  // the MFMAs and fragment reads are scheduled in (the re-read is 4 % more bytes per tile; the
+  // Qwen3-shaped layer on MXFP4 weights went from 1.57 to 1.51 ms).  The 32-row tiles stream
+  // weights, where the extra bytes cost more than the branches (1 % on the decode gate-up).
+  constexpr bool REREAD = GE::A8 && TM * TN >= 8;
   auto issue_a = [&](int lk, int slot) {
-    const bool valid = lk < ktn;
+    const bool valid = REREAD || lk < ktn;
+    if constexpr (REREAD) lk = lk < ktn ? lk : ktn - 1;
     char* sa = a_slots + slot * A_STAGE;
     const int kb = valid ? (kt0 + lk) * ROWB : 0;
 #pragma unroll
@@ -695,7 +702,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
     }
   };
   auto issue_b = [&](int lk, int bslot) {
-    const bool valid = lk < ktn;
+    const bool valid = REREAD || lk < ktn;
+    if constexpr (REREAD) lk = lk < ktn ? lk : ktn - 1;
     char* sb = b_slots + bslot * B_STAGE;
     const int kbw = valid ? (kt0 + lk) * (GE::MX4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
@@ -718,7 +726,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   // weight-side loads [i0, i1) of step lk into slot bslot: the weight tile's B_LOADS, then (E2M1
   // weights) its SC_LOADS scale loads
   auto issue_b_part = [&](int lk, int bslot, int i0, int i1) {
-    const bool valid = lk < ktn;
+    const bool valid = REREAD || lk < ktn;
+    if constexpr (REREAD) lk = lk < ktn ? lk : ktn - 1;
     char* sb = b_slots + bslot * B_STAGE;
     const int kbw = valid ? (kt0 + lk) * (GE::MX4 ? 32 * B_ROWB : B_ROWB) : 0;
 #pragma unroll
