@@ -280,8 +280,8 @@ using ShapeMxfp4 = TileShape<32, 256, 1, 4, 2, 128>;
 // MXFP8 token rows with MXFP4 weights: the same 32-row blocking and two stages; a stage's token
 // rows are one 128-byte line each (128 E4M3 codes) plus a scale dword (46 KB for both stages)
 using ShapeMx4A8 = TileShape<32, 256, 1, 4, 2, 128, 2, 1>;
-// ... and for groups of >= 128 rows on average, 256 x 256 tiles with three stages of both
-// operands (52 KB each).  Wavefront tiles of 64 token rows x 128 columns: per 64-k MFMA step a
+// ... and for groups of >= 128 rows on average, 256 x 256 tiles with two stages of the token
+// rows (34 KB each) and three of the weights (18 KB each).  Wavefront tiles of 64 token rows x 128 columns: per 64-k MFMA step a
 // token block takes two 16-byte LDS reads per lane and a weight block one, so four weight blocks
 // and two token blocks (10 reads for 8 MFMAs) beat the 128 x 64 split of the bf16 shape
 using PrefillShapeMx4A8 = TileShape<256, 256, 4, 2, 2, 128, 3, 1>;
@@ -775,13 +775,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
   i32x8 fa8[2][TM];
   i32x4 fb4[2][TN];
   int sca[2][TM], scb[2][TN];
-  // Large MXFP8 wavefront tiles keep one set of token fragments (the registers of a second set
-  // do not fit beside 128 accumulators at two wavefronts per SIMD): the token fragments of the
-  // next MFMA step are read after this step's MFMAs have consumed theirs
-  constexpr bool A1 = GE::A8 && TM * TN >= 8;
   // NV: the wavefront's token blocks that hold rows of the tile (the others are skipped)
-  // part: 0 both operands, 1 the token rows only, 2 the weights only (MXFP8 token rows)
-  auto read_frags = [&](auto nv, const char* sta, const char* st, int kk, int buf, int part = 0) {
+  auto read_frags = [&](auto nv, const char* sta, const char* st, int kk, int buf) {
     constexpr int NV = decltype(nv)::value;
     if constexpr (GE::A8) {
       // sub-step kk covers k 64kk .. 64kk + 63 of the stage.  Token lane: k 64kk + 16hi .. + 15
@@ -791,21 +786,18 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
       const int blk = 2 * kk + hi;
       const uint32_t c0 = (uint32_t)(((4 * kk + hi) ^ sw) * 16);
       const uint32_t c1 = (uint32_t)(((4 * kk + 2 + hi) ^ sw) * 16);
-      const int abuf = A1 ? 0 : buf;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        if (part == 2) break;
         const char* ra = sta + a_frag + i * 32 * ROWB;
         const i32x4 lo = *(const i32x4*)(ra + c0), up = *(const i32x4*)(ra + c1);
-        fa8[abuf][i] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        fa8[buf][i] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         const uint32_t s4 =
             *(const uint32_t*)(sta + SH::A_BYTES + ((wm * SH::WTM) / 32 + i) * 256 + l32 * 4);
-        sca[abuf][i] = (int)((s4 >> (8 * blk)) & 0xffu);
+        sca[buf][i] = (int)((s4 >> (8 * blk)) & 0xffu);
       }
       const uint32_t woff = (uint32_t)((blk ^ swb) * 16);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if (part == 1) break;
         fb4[buf][j] = *(const i32x4*)(st + b_frag + woff + j * 32 * B_ROWB);
         const uint32_t s4 =
             *(const uint32_t*)(st + SC_OFF + ((wn * SH::WTN) / 32 + j) * 256 + l32 * 4);
@@ -852,9 +844,8 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
           // second E4M3 (format 0), each with its lane's E8M0 scale
           const i32x4 w = fb4[buf][j];
           const i32x8 wa = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
-          const int abuf = A1 ? 0 : buf;
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wa, fa8[abuf][i], acc[i][j], 4, 0, 0, scb[buf][j], 0, sca[abuf][i]);
+              wa, fa8[buf][i], acc[i][j], 4, 0, 0, scb[buf][j], 0, sca[buf][i]);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
         }
@@ -874,12 +865,12 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         if (kk < KK - 1) {
-          if constexpr (!A1) read_frags(nv, cura, curb, kk + 1, (kk + 1) & 1);
+          read_frags(nv, cura, curb, kk + 1, (kk + 1) & 1);
         } else {
           wait_vmcnt<GE::WAIT>();  // step lk + 1 landed (this wavefront's share)
           wait_lgkmcnt<0>();       // this wavefront's reads of step lk returned
           barrier_keep_loads();    // ... and everyone else's
-          if constexpr (!A1) read_frags(nv, nxta, nxtb, 0, 0);
+          read_frags(nv, nxta, nxtb, 0, 0);
           if constexpr (S < SB) issue_a(lk + S, lk % S);
           else issue_both(lk + S, lk % S, lk + SB, lk % SB);
         }
@@ -895,11 +886,7 @@ __global__ __launch_bounds__(SH::THREADS) void gemm_kernel(GroupedGemm p) {
           if (kk < BSPAN && lk > 0)
             issue_b_part(lk - 1 + SB, (lk - 1) % SB, kk * BPER, (kk + 1) * BPER);
         }
-        mfmas(nv, A1 ? 0 : kk & 1);
-        if constexpr (A1) {  // the fragments of the next MFMA step, into the freed registers
-          if (kk < KK - 1) read_frags(nv, cura, curb, kk + 1, 0);
-          else read_frags(nv, nxta, nxtb, 0, 0);
-        }
+        mfmas(nv, kk & 1);
         if constexpr (GE::A8) {
           // few, long MFMAs per sub-step: the next sub-step's reads (3 per token block, 2 per
           // weight block) and the sub-step's global loads spread evenly over them
