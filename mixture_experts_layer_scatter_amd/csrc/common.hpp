@@ -82,8 +82,8 @@ struct PermuteArgs {
   int n, k, E, T;
   int capacity;            // < 0 unlimited
   int ntiles;              // ceil(n / kSlotTile)
-  int32_t* tile_hist;      // [E * ntiles]
-  int32_t* tile_base;      // [E * ntiles]
+  int32_t* tile_hist;      // [ntiles, E] per-tile counts
+  int32_t* tile_base;      // [ntiles, E] per-tile starting ranks
   int32_t* raw;            // [E]
   int32_t* counts;         // [E]   kept
   int32_t* offsets;        // [E+2] (E+1 used when shared_rows > 0)

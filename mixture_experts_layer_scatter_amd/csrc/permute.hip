@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(PermuteArgs a) {
   }
   __syncthreads();
   for (int e = threadIdx.x; e < a.E; e += blockDim.x)
-    a.tile_hist[(int64_t)e * a.ntiles + tile] = hist[e];
+    a.tile_hist[(int64_t)tile * a.E + e] = hist[e];
 }
 
 // block-wide exclusive scan of up to 2 * 1024 values (2 per thread), returns the total
@@ -88,12 +88,20 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(PermuteArgs a) {
   const int tid = threadIdx.x;
   int my_drop = 0;
   for (int e = tid; e < a.E; e += blockDim.x) {
+    // the tiles' counts of expert e, 16 loads in flight at a time (tile-major arrays: a
+    // wavefront's lanes read neighbouring experts of one tile)
+    const int32_t* __restrict__ hist = a.tile_hist + e;
+    int32_t* __restrict__ base = a.tile_base + e;
     int run = 0;
-    for (int tile = 0; tile < a.ntiles; ++tile) {
-      const int64_t i = (int64_t)e * a.ntiles + tile;
-      const int h = a.tile_hist[i];
-      a.tile_base[i] = run;
-      run += h;
+    for (int t0 = 0; t0 < a.ntiles; t0 += 16) {
+      int h[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h[j] = t0 + j < a.ntiles ? hist[(int64_t)(t0 + j) * a.E] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (t0 + j < a.ntiles) base[(int64_t)(t0 + j) * a.E] = run;
+        run += h[j];
+      }
     }
     a.raw[e] = run;
     const int kp = (a.capacity >= 0 && run > a.capacity) ? a.capacity : run;
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(PermuteArgs a) {
   __syncthreads();
   // running start of each wavefront: tile base + earlier wavefronts of this tile
   for (int e = tid; e < a.E; e += blockDim.x) {
-    int b = a.tile_base[(int64_t)e * a.ntiles + tile];
+    int b = a.tile_base[(int64_t)tile * a.E + e];
     for (int w = 0; w < 4; ++w) {
       const int h = run[w][e];
       run[w][e] = b;
@@ -233,14 +241,18 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
                                                         int nt1, int32_t* __restrict__ start1,
                                                         int4* __restrict__ info1) {
   __shared__ int32_t buf[2 * 1024];
+  __shared__ int32_t offs[2 * 1024 + 1];
   __shared__ int32_t tmp[1024 / kWave + 1];
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  for (int g = threadIdx.x; g <= G; g += blockDim.x) offs[g] = offsets[g];
+  __syncthreads();
   for (int pass = 0; pass < 2; ++pass) {
     const int bm = pass ? bm1 : bm0, nt = pass ? nt1 : nt0;
     int32_t* out = pass ? start1 : start0;
     int4* info = pass ? info1 : info0;
     if (!out) continue;
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
-      const int rows = offsets[g + 1] - offsets[g];
+      const int rows = offs[g + 1] - offs[g];
       buf[g] = (rows + bm - 1) / bm * nt;
     }
     __syncthreads();
@@ -248,17 +260,12 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     for (int g = threadIdx.x; g < G; g += blockDim.x) out[g] = buf[g];
     if (threadIdx.x == 0) out[G] = total;
     if (info) {
-      __syncthreads();
-      // tile t belongs to the largest g with tile_start[g] <= t (groups without tiles share
-      // their start with the next group, and never hold the largest such g for a t below it)
-      for (int t = threadIdx.x; t < total; t += blockDim.x) {
-        int lo = 0, hi = G;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (buf[mid] <= t) lo = mid;
-          else hi = mid;
-        }
-        info[t] = make_int4(lo, buf[lo], offsets[lo], offsets[lo + 1] - offsets[lo]);
+      // tiles [buf[g], buf[g + 1]) belong to group g; wavefront w fills those of groups w,
+      // w + 16, ... (a group without tiles writes nothing)
+      for (int g = wid; g < G; g += blockDim.x / kWave) {
+        const int t0 = buf[g], t1 = g + 1 < G ? buf[g + 1] : total;
+        const int4 v = make_int4(g, t0, offs[g], offs[g + 1] - offs[g]);
+        for (int t = t0 + lane; t < t1; t += kWave) info[t] = v;
       }
     }
     __syncthreads();

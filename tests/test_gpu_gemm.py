@@ -155,3 +155,43 @@ def test_combine(dtype, shared, k):
         mag += np.abs(moe_synth.widen(ys))
     bound = 1e-6 * mag + (2.0 ** -8 * np.abs(ref) if dtype == "bf16" else 0)
     assert (np.abs(got - ref) <= bound + 1e-30).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_combine_split_and_per_token_kernels_agree(dtype):
+    """Below 2048 tokens a token's vector is split over several blocks (one 16-byte chunk per
+    thread); from 2048 up one block takes a whole token.  Both add the same terms in the same
+    order: the first 2047 tokens of a 2100-token batch give the same bits either way, and the
+    whole batch is checked against the oracle."""
+    need_gpu()
+    rng = np.random.default_rng(77)
+    T, H, k = 2100, 2304, 8                 # 288 bf16 chunks a row: two blocks, the second ragged
+    R = T * k - 3000
+    if dtype == "bf16":
+        yp = bf16_normal(rng, (T * k, H))
+        ys = bf16_normal(rng, (T, H))
+    else:
+        yp = rng.standard_normal((T * k, H), dtype=np.float32)
+        ys = rng.standard_normal((T, H), dtype=np.float32)
+    pos = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    pos[pos >= R] = -1
+    w = rng.random((T, k), dtype=np.float32)
+    gyp, gys, gpos, gw = dev(yp), dev(ys), dev(pos), dev(w)
+    d = moe.Dims(T=T, H=H, E=16, k=k, I=64, dtype=dtype)
+    y = torch.empty((T, H), dtype=d.torch_dtype, device="cuda")
+    moe.combine(d, gyp, gpos, gw, gys, y)
+    Ts = 2047
+    ds = moe.Dims(T=Ts, H=H, E=16, k=k, I=64, dtype=dtype)
+    y2 = torch.empty((Ts, H), dtype=d.torch_dtype, device="cuda")
+    moe.combine(ds, gyp, gpos[:Ts].contiguous(), gw[:Ts].contiguous(), gys[:Ts].contiguous(), y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:Ts], y2), "split and per-token combine differ"
+    got = f64(y)
+    ref = oracle.combine(moe_synth.widen(yp), pos, w.astype(np.float64), moe_synth.widen(ys))
+    mag = np.abs(moe_synth.widen(ys))
+    ypw = np.abs(moe_synth.widen(yp))
+    for j in range(k):
+        ok = pos[:, j] >= 0
+        mag[ok] += np.abs(w[ok, j:j + 1].astype(np.float64)) * ypw[pos[ok, j]]
+    bound = 1e-6 * mag + (2.0 ** -8 * np.abs(ref) if dtype == "bf16" else 0)
+    assert (np.abs(got - ref) <= bound + 1e-30).all()
