@@ -15,6 +15,9 @@
 // bases, so a slot's rank is the number of earlier slots (= earlier tokens)
 // routed to the same expert.  Ranks at or above the capacity are dropped;
 // the others land at row offsets[e] + rank.  Integer work only: bit-exact.
+// Batches of at most kSmallSlots slots take all three passes in one block of 16
+// wavefronts (256 slots each, per-wavefront counts in LDS): the same ranks, one
+// launch instead of three.
 #include "common.hpp"
 
 namespace moe {
@@ -197,7 +200,105 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(PermuteArgs a) {
   }
 }
 
+// ---- small batches: histogram, scan and ranks in one block ---------------------------------
+// 1024 threads = 16 wavefronts; wavefront w owns slots [w*256, w*256+256) and walks them in 4
+// chunks of 64 in order, as a tile's wavefronts do in perm_rank_kernel; its per-expert counts,
+// then their running starts, live in LDS.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallSlots = kSmallWaves * 256;
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(PermuteArgs a) {
+  __shared__ int32_t run[kSmallWaves][kMaxExperts];
+  __shared__ int32_t kept[2 * 1024];
+  __shared__ int32_t dropped_part[1024 / kWave];
+  __shared__ int32_t tmp[1024 / kWave + 1];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  for (int i = tid; i < kSmallWaves * a.E; i += blockDim.x) run[i / a.E][i % a.E] = 0;
+  __syncthreads();
+  const int s_wave = wid * 256;
+  for (int c = 0; c < 4; ++c) {
+    const int s = s_wave + c * kWave + lane;
+    if (slot_active(a, s)) atomicAdd(&run[wid][a.ids[s]], 1);
+  }
+  __syncthreads();
+  // per expert: the wavefronts' starting ranks (earlier wavefronts = earlier slots), the raw
+  // count and the kept count
+  int my_drop = 0;
+  for (int e = tid; e < a.E; e += blockDim.x) {
+    int b = 0;
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int h = run[w][e];
+      run[w][e] = b;
+      b += h;
+    }
+    a.raw[e] = b;
+    const int kp = (a.capacity >= 0 && b > a.capacity) ? a.capacity : b;
+    kept[e] = kp;
+    a.counts[e] = kp;
+    my_drop += b - kp;
+  }
+  __syncthreads();
+  const int R = block_exclusive_scan2<1024>(kept, tmp, a.E);  // kept[e] = offsets[e] from here
+  for (int e = tid; e < a.E; e += blockDim.x) a.offsets[e] = kept[e];
+  if (tid == 0) {
+    a.offsets[a.E] = R;
+    if (a.shared_rows > 0) a.offsets[a.E + 1] = R + a.shared_rows;
+  }
+  if (a.shared_rows > 0 && a.row_token)
+    for (int t = tid; t < a.shared_rows; t += blockDim.x) a.row_token[R + t] = t;
+  int v = my_drop;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  if (lane == 0) dropped_part[wid] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int sum = 0;
+    for (int i = 0; i < 1024 / kWave; ++i) sum += dropped_part[i];
+    if (a.n_dropped) *a.n_dropped = sum;
+  }
+  if (!a.dropped && !a.pos) return;  // counts only (the same for every thread)
+  int nbits = 0;
+  while ((1 << nbits) < a.E) ++nbits;
+  for (int c = 0; c < 4; ++c) {
+    const int s = s_wave + c * kWave + lane;
+    const bool in = s < a.n;
+    const bool active = slot_active(a, s);
+    const int e = active ? a.ids[s] : 0;
+    // lanes of this chunk routed to the same expert
+    uint64_t peers = __ballot(active);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bal = __ballot((e >> b) & 1);
+      peers &= ((e >> b) & 1) ? bal : ~bal;
+    }
+    if (active) {
+      const int base = run[wid][e];
+      const int rank = base + __popcll(peers & lanemask_lt(lane));
+      const bool drop = a.capacity >= 0 && rank >= a.capacity;
+      if (a.dropped) a.dropped[s] = drop ? 1 : 0;
+      if (a.pos) {
+        if (drop) {
+          a.pos[s] = -1;
+        } else {
+          const int row = kept[e] + rank;
+          a.pos[s] = row;
+          if (a.row_token) a.row_token[row] = s / a.k;
+        }
+      }
+      // the highest lane of the group advances the running count
+      if ((peers >> lane) == 1ull) run[wid][e] = base + __popcll(peers);
+    } else if (in) {
+      if (a.dropped) a.dropped[s] = 1;
+      if (a.pos) a.pos[s] = -1;
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  if (a.n > 0 && a.n <= kSmallSlots) {
+    perm_small_kernel<<<1, 1024, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (a.n <= 0) {
     // no slots: every count is zero
     perm_scan_kernel<<<1, 1024, 0, s>>>(a);

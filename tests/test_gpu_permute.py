@@ -50,10 +50,12 @@ def _ids(rng, T, E, k, hot=0):
     return out
 
 
-# (9000, 128, 4): 36000 slots in 36 tiles of 1024, so the scan's per-expert walk over the tiles
-# takes three batches of loads (16, 16, 4)
+# Up to 4096 slots one block takes all three passes; (2048, 16, 2) is that limit and
+# (4097, 9, 1) one slot past it.  (9000, 128, 4): 36000 slots in 36 tiles of 1024, so the scan's
+# per-expert walk over the tiles takes three batches of loads (16, 16, 4)
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (5, 3, 2), (50, 5, 2), (1000, 8, 2),
-                                   (3000, 64, 2), (777, 1024, 3), (2049, 7, 7), (9000, 128, 4)])
+                                   (3000, 64, 2), (777, 1024, 3), (2049, 7, 7), (2048, 16, 2),
+                                   (4097, 9, 1), (9000, 128, 4)])
 def test_permute_bit_exact(T, E, k):
     need_gpu()
     log(f"permute T={T} E={E} k={k}")
