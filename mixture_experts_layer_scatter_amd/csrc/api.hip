@@ -173,8 +173,10 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 // ---- step implementations shared by the step-wise and fused calls --------------------------
 
 // splits > 1 needs `part` with room for splits * T * E floats
+// With reduce = false a split gate stops at the partial sums in `part` (the route kernel adds
+// them up).
 hipError_t run_gate(const moe_dims_t* d, const void* x, const void* wg, float* logits,
-                    hipStream_t s, int splits = 1, float* part = nullptr) {
+                    hipStream_t s, int splits = 1, float* part = nullptr, bool reduce = true) {
   GroupedGemm p = {};
   p.a = x;
   p.a_rows = d->T;
@@ -193,7 +195,7 @@ hipError_t run_gate(const moe_dims_t* d, const void* x, const void* wg, float* l
     p.ksplit = splits;
     p.c_split_stride = (int64_t)d->T * d->E;
     hipError_t e = launch_gemm_bf16(GEMM_GATE, p, d->T, num_cus(), s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !reduce) return e;
     return launch_splitk_reduce(part, splits, (int64_t)d->T * d->E, logits, s);
   }
   int bm, nt;
@@ -646,9 +648,15 @@ moe_status_t layer_forward_impl(const moe_dims_t* d, const void* x, const void* 
   void* const* ev = dbg ? dbg->events : nullptr;
   // 1. gate  2. softmax / top-k / renormalise
   MOE_TRY(mark(ev, MOE_EV_START, s));
-  MOE_TRY(run_gate(d, x, wg, logits, s, gate_splits(d), at<float>(ws, L.gate_part)));
+  // a split gate leaves partial sums; the route kernel adds them (in the reduction's order) and
+  // writes the logits
+  const int gs = gate_splits(d);
+  float* gpart = at<float>(ws, L.gate_part);
+  const bool fused_sum = d->dtype == MOE_BF16 && gs > 1;
+  MOE_TRY(run_gate(d, x, wg, logits, s, gs, gpart, !fused_sum));
   MOE_TRY(mark(ev, MOE_EV_GATE, s));
-  MOE_TRY(launch_route(logits, bias, T, E, k, d->renormalize, d->bias_mode, ids, w, s));
+  MOE_TRY(launch_route(logits, bias, T, E, k, d->renormalize, d->bias_mode, ids, w, s,
+                       fused_sum ? gpart : nullptr, gs, fused_sum ? logits : nullptr));
   MOE_TRY(mark(ev, MOE_EV_ROUTE, s));
   // 3. count, capacity, scan, stable scatter (rows of the folded shared expert appended)
   PermuteArgs a = permute_args(d, L, ws);

@@ -66,9 +66,12 @@ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Launchers (each returns hipGetLastError() of its launch(es)).
 // ---------------------------------------------------------------------------
 
-// route.hip: one wavefront per token; softmax, top-k, renormalise.
+// route.hip: one wavefront per token; softmax, top-k, renormalise.  With `part` (a split gate's
+// S partial sums, [S, T, E]) the logits are first summed from it, part 0 then 1 .. S - 1 as the
+// split-K reduction adds them, and written to logits_out; else they are read from `logits`.
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
-                        int renormalize, int bias_mode, int32_t* ids, float* w, hipStream_t s);
+                        int renormalize, int bias_mode, int32_t* ids, float* w, hipStream_t s,
+                        const float* part = nullptr, int S = 1, float* logits_out = nullptr);
 
 // stats.hip: load statistics of the per-expert pick counts (raw, after launch_permute's scan)
 // and the next balancing bias

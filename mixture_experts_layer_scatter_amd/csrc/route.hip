@@ -51,16 +51,22 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+constexpr int kRouteMaxSplits = 16;  // the most partial sums a split gate leaves
+
+// With gpart != null the logits are the sum of a split gate's S partials (part 0, then 1 .. S - 1:
+// the order of the split-K reduction, so the same bits), written to logits_out on the way.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int renormalize, int sel_only,
                                                     int32_t* __restrict__ ids,
-                                                    float* __restrict__ w) {
+                                                    float* __restrict__ w,
+                                                    const float* __restrict__ gpart, int S,
+                                                    float* __restrict__ logits_out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // whole wavefront leaves together
-  const float* row = logits + (int64_t)t * E;
+  const int64_t row0 = (int64_t)t * E, n = (int64_t)T * E;
 
   // key: what the experts are ranked by; val: what the softmax is taken of
   float key[EPL], val[EPL];
@@ -70,7 +76,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int e = s * kWave + lane;
     float v = -INFINITY, l = -INFINITY;
     if (e < E) {
-      l = row[e];
+      if (gpart) {
+        // every partial's load goes out before the first add
+        float pv[kRouteMaxSplits];
+#pragma unroll
+        for (int q = 0; q < kRouteMaxSplits; ++q) pv[q] = q < S ? gpart[q * n + row0 + e] : 0.f;
+        l = pv[0];
+#pragma unroll
+        for (int q = 1; q < kRouteMaxSplits; ++q)
+          if (q < S) l += pv[q];
+        logits_out[row0 + e] = l;
+      } else {
+        l = logits[row0 + e];
+      }
       v = bias ? l + bias[e] : l;  // one fp32 add
     }
     key[s] = v;
@@ -160,22 +178,24 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
-                        int renormalize, int bias_mode, int32_t* ids, float* w, hipStream_t s) {
+                        int renormalize, int bias_mode, int32_t* ids, float* w, hipStream_t s,
+                        const float* part, int S, float* logits_out) {
+  if (part && (S < 1 || S > kRouteMaxSplits || !logits_out)) return hipErrorInvalidValue;
   const int sel = bias != nullptr && bias_mode == 1;
   if (T <= 0) return hipSuccess;
   const int per_block = 4;  // tokens (wavefronts) per block
   dim3 grid(ceil_div(T, per_block)), block(per_block * kWave);
   const int epl = ceil_div(E, kWave);
   if (epl <= 1)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
+    route_kernel<1><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w, part, S, logits_out);
   else if (epl <= 2)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
+    route_kernel<2><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w, part, S, logits_out);
   else if (epl <= 4)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
+    route_kernel<4><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w, part, S, logits_out);
   else if (epl <= 8)
-    route_kernel<8><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
+    route_kernel<8><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w, part, S, logits_out);
   else
-    route_kernel<16><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w);
+    route_kernel<16><<<grid, block, 0, s>>>(logits, bias, T, E, k, renormalize, sel, ids, w, part, S, logits_out);
   return hipGetLastError();
 }
 
